@@ -1,0 +1,135 @@
+/*
+ * oracle.c -- plain double-precision CPU oracle for the single-precision
+ * matrix product C = A x B.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test-suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no source with the HIP library.
+ *
+ * What it computes.  The plain definition of the product: for an M x K
+ * matrix A and a K x N matrix B, entry (i, j) of C is the sum over
+ * k = 0 .. K-1 of A(i,k) * B(k,j)  [article "硬件加速原理：CUDA核函数优化矩阵
+ * 乘法的内存访问模式", section "矩阵乘法的计算特性" (computational properties of
+ * matrix multiplication), the summation formula; also the textbook chapter
+ * "4. 矩阵乘法性能优化", opening paragraph].  Storage is row-major with
+ * explicit leading dimensions, as in the blog "【infra之路】03_动手写 CUDA
+ * Kernel", v1 Naive kernel (A indexed row*width+k, B indexed k*width+col).
+ *
+ * Precision.  Inputs are IEEE single precision.  Each product of two floats
+ * is formed in double, where it is exact (24 + 24 significand bits fit in
+ * 53), and the products are summed in double in ascending k.  The blog's own
+ * CPU check sums in float; that is deliberately not followed.  Alongside the
+ * value the oracle returns S(i,j) = sum_k |A(i,k) * B(k,j)|, the scale that
+ * the per-element tolerance |C - Cref| <= 1e-5 * S + 1e-6 is stated in.
+ *
+ * Build: gcc -O2 -fPIC -shared -ffp-contract=off -fno-fast-math -fopenmp.
+ * -ffp-contract=off keeps every multiply and add separately rounded; OpenMP
+ * only splits whole rows between threads, so the arithmetic of each entry is
+ * the same for any thread count.
+ */
+#include <stddef.h>
+#include <stdint.h>
+#include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG -1
+
+static int dims_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb)
+{
+    if (M < 0 || N < 0 || K < 0) return 0;
+    if (lda < (K > 1 ? K : 1)) return 0;
+    if (ldb < (N > 1 ? N : 1)) return 0;
+    return 1;
+}
+
+/*
+ * Full product.  Cref (M x N, leading dimension ldr) receives the double sums;
+ * Sabs (same shape, leading dimension lds) receives the absolute-product sums
+ * and may be NULL.  Loop order i, k, j: for a fixed (i, j) the terms are
+ * still added in ascending k, so each entry equals the textbook i, j, k dot
+ * product bit for bit (oracle_entries_f64 below computes exactly that).
+ * nthreads <= 0 lets OpenMP choose.
+ */
+int oracle_sgemm_f64(int64_t M, int64_t N, int64_t K,
+                     const float *A, int64_t lda,
+                     const float *B, int64_t ldb,
+                     double *Cref, int64_t ldr,
+                     double *Sabs, int64_t lds,
+                     int nthreads)
+{
+    if (!dims_ok(M, N, K, lda, ldb)) return ORACLE_BAD_ARG;
+    if (ldr < (N > 1 ? N : 1)) return ORACLE_BAD_ARG;
+    if (Sabs && lds < (N > 1 ? N : 1)) return ORACLE_BAD_ARG;
+    if (M == 0 || N == 0) return ORACLE_OK;
+    if (!Cref || (K > 0 && (!A || !B))) return ORACLE_BAD_ARG;
+
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < M; ++i) {
+        double *c = Cref + i * ldr;
+        double *s = Sabs ? Sabs + i * lds : NULL;
+        for (int64_t j = 0; j < N; ++j) c[j] = 0.0;
+        if (s)
+            for (int64_t j = 0; j < N; ++j) s[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = (double)A[i * lda + k];
+            const float *b = B + k * ldb;
+            if (s) {
+                for (int64_t j = 0; j < N; ++j) {
+                    const double p = a * (double)b[j];
+                    c[j] += p;
+                    s[j] += fabs(p);
+                }
+            } else {
+                for (int64_t j = 0; j < N; ++j) c[j] += a * (double)b[j];
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Selected entries.  For e < n, entry (I[e], J[e]) is the ascending-k dot
+ * product of row I[e] of A with column J[e] of B, in double; sabs may be NULL.
+ * Used where the full product would take too long on the host.
+ */
+int oracle_entries_f64(int64_t M, int64_t N, int64_t K,
+                       const float *A, int64_t lda,
+                       const float *B, int64_t ldb,
+                       int64_t n, const int64_t *I, const int64_t *J,
+                       double *cref, double *sabs)
+{
+    if (!dims_ok(M, N, K, lda, ldb) || n < 0) return ORACLE_BAD_ARG;
+    if (n > 0 && (!I || !J || !cref)) return ORACLE_BAD_ARG;
+    for (int64_t e = 0; e < n; ++e)
+        if (I[e] < 0 || I[e] >= M || J[e] < 0 || J[e] >= N) return ORACLE_BAD_ARG;
+    if (K > 0 && n > 0 && (!A || !B)) return ORACLE_BAD_ARG;
+
+    for (int64_t e = 0; e < n; ++e) {
+        const int64_t i = I[e], j = J[e];
+        double acc = 0.0, sab = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double p = (double)A[i * lda + k] * (double)B[k * ldb + j];
+            acc += p;
+            sab += fabs(p);
+        }
+        cref[e] = acc;
+        if (sabs) sabs[e] = sab;
+    }
+    return ORACLE_OK;
+}
+
+/* Threads OpenMP would use by default; 1 when built without OpenMP. */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
