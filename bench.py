@@ -1,0 +1,180 @@
+"""Throughput of the single-precision product C = A x B on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--variant V] [--no-cpu-baseline] [--no-secondary]
+
+One step is one call of sgemm_run on the 8192^3 workload (uniform[-1, 1)
+inputs from seed 4, already resident in HBM).  W untimed calls, then exactly
+K calls between two synchronisations, timed with HIP events recorded on the
+stream the kernels run on.  Prints one JSON line.  The 2048^3 workload is
+timed the same way and reported under "secondary".
+
+The CPU baseline is the oracle (double-precision triple loop) timed on the
+host cores on a bounded sample of the same workload: the first R rows of C,
+with R chosen so the sample takes roughly 10-20 s; its rate is scaled to the
+same unit (TFLOP/s of the single-precision product it checks).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP32 SGEMM TFLOPS at 2048³ and 8192³ on 1 MI355X; % of FP32 MFMA peak"
+PEAK_TFLOPS = 157.3    # MI355X dense FP32 matrix-core peak (published)
+HEADLINE = "sgemm_8192x8192x8192_uniform_seed4"
+SECONDARY = "sgemm_2048x2048x2048_uniform_seed2"
+COUNTERS = os.path.join(ROOT, "profiles", "mfma_gemm_8192_hbm_counters.json")
+
+
+def kernel_source_digest() -> str:
+    """Digest of the HIP sources; HBM counters are valid only for this digest."""
+    csrc = os.path.join(ROOT, "dense_fp32_matrix_03_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none for this workload or the kernels changed since."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("workload") != workload or c.get("source_sha256") != kernel_source_digest():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def time_gpu(w, variant: str, steps: int, warmup: int):
+    import torch
+
+    import dense_fp32_matrix_03_amd as sg
+    from dense_fp32_matrix_03_amd import inputs
+
+    A, B = inputs.make_inputs(w)
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(B).cuda()
+    del A, B
+    dC = torch.empty((w.M, w.ldc), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+
+    def step():
+        sg.sgemm_run_variant(variant, w.M, w.N, w.K, dA, w.lda, dB, w.ldb, dC, w.ldc, h)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    finite = bool(torch.isfinite(dC[:, :w.N]).all().item())
+    del dA, dB, dC
+    torch.cuda.empty_cache()
+    return ms, finite
+
+
+def cpu_baseline(w, target_s: float = 12.0):
+    """Time the oracle on the first R rows of the workload (no GPU involved)."""
+    import numpy as np
+
+    import oracle
+    from dense_fp32_matrix_03_amd import inputs
+
+    A, B = inputs.make_inputs(w)
+    threads = oracle.max_threads()
+    rows = 8
+    while True:
+        t = time.perf_counter()
+        oracle.sgemm_f64(np.ascontiguousarray(A[:rows]), B, K=w.K, N=w.N, want_sabs=False,
+                         threads=threads)
+        dt = time.perf_counter() - t
+        if dt >= target_s or rows >= w.M:
+            break
+        rows = min(w.M, max(rows * 2, int(rows * target_s / max(dt, 1e-3) * 1.05)))
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} of {w.M} rows of C (= {rows}x{w.N}x{w.K}), double "
+                      f"accumulation, {dt:.1f} s on {threads} threads"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description="single-precision GEMM throughput on MI355X")
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--variant", default="mfma", help="kernel variant (default: sgemm_run's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(the product shards by rows of C with B replicated; not built here)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import dense_fp32_matrix_03_amd as sg
+    from dense_fp32_matrix_03_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    sg.sgemm_create()
+    w = inputs.BY_NAME[a.workload]
+    variant = sg.VARIANTS[a.variant] if a.variant in sg.VARIANTS else int(a.variant)
+
+    ms, finite = time_gpu(w, variant, a.steps, a.warmup)
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda,
+                   "ldb": w.ldb, "ldc": w.ldc, "dist": w.dist, "seed": w.seed,
+                   "variant": sg.sgemm_variant_name(variant)},
+        "pct_of_peak": round(100 * tflops / PEAK_TFLOPS, 2),
+        "output_finite": finite,
+    }
+    traffic = measured_traffic(w.name)
+    out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS, 4),
+                       "traffic": traffic}
+    if not a.no_secondary and w.name != SECONDARY:
+        w2 = inputs.BY_NAME[SECONDARY]
+        ms2, finite2 = time_gpu(w2, variant, max(a.steps, 50), max(a.warmup, 10))
+        t2 = w2.flops / (ms2 * 1e-3) / 1e12
+        out["secondary"] = {"workload": w2.name, "value": round(t2, 3), "unit": "TFLOP/s",
+                            "ms_per_step": round(ms2, 5),
+                            "pct_of_peak": round(100 * t2 / PEAK_TFLOPS, 2),
+                            "output_finite": finite2}
+    sg.sgemm_destroy()
+    out["cpu_baseline"] = None if a.no_cpu_baseline else cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

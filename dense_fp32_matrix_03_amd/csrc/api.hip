@@ -1,0 +1,195 @@
+// api.hip -- the C interface declared in include/sgemm.h: argument checks,
+// device check, and the choice of kernel configuration for each call.
+#include <stdint.h>
+
+#include <atomic>
+#include <cstring>
+#include <mutex>
+
+#include "dispatch.hpp"
+#include "sgemm.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+  bool known = false;
+  bool supported = false;
+  int cus = 0;
+};
+
+std::mutex g_mu;
+int g_refs = 0;
+std::atomic<int> g_ready{0};
+DeviceInfo g_dev[kMaxDevices];
+
+// Query (once) and cache what the dispatcher needs to know about device d.
+int device_info(int d, DeviceInfo *out) {
+  if (d < 0 || d >= kMaxDevices) return SGEMM_ERR_UNSUPPORTED_DEVICE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  DeviceInfo &di = g_dev[d];
+  if (!di.known) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, d) != hipSuccess) return SGEMM_ERR_HIP;
+    di.supported = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    di.cus = prop.multiProcessorCount;
+    di.known = true;
+  }
+  *out = di;
+  return di.supported ? SGEMM_OK : SGEMM_ERR_UNSUPPORTED_DEVICE;
+}
+
+int current_device_info(DeviceInfo *out) {
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess) return SGEMM_ERR_HIP;
+  return device_info(d, out);
+}
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+// Shared argument checks of every product entry point.
+int check_args(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+               int64_t ldb, const float *C, int64_t ldc) {
+  if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_INVALID_VALUE;
+  if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+    return SGEMM_ERR_INVALID_VALUE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return SGEMM_ERR_TOO_LARGE;
+  // One work-group per 16 x 16 tile must still fit a 32-bit grid.
+  if (((M + 15) / 16) * ((N + 15) / 16) > kMaxDim) return SGEMM_ERR_TOO_LARGE;
+  if (M == 0 || N == 0) return SGEMM_OK;
+  if (!C) return SGEMM_ERR_INVALID_VALUE;
+  if (K > 0 && (!A || !B)) return SGEMM_ERR_INVALID_VALUE;
+  return SGEMM_OK;
+}
+
+inline bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Matrix-core block tile for a shape: the largest tile that still gives at
+// least one work-group per compute unit, else the smallest.
+sgemm::MfmaTile choose_tile(int64_t M, int64_t N, int cus) {
+  auto tiles = [&](int64_t t) { return ((M + t - 1) / t) * ((N + t - 1) / t); };
+  if (tiles(256) >= cus) return sgemm::MfmaTile::T256;
+  if (tiles(128) >= cus) return sgemm::MfmaTile::T128;
+  return sgemm::MfmaTile::T64;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sgemm_create(void) {
+  DeviceInfo di;
+  const int rc = current_device_info(&di);
+  if (rc != SGEMM_OK) return rc;
+  std::lock_guard<std::mutex> lk(g_mu);
+  ++g_refs;
+  g_ready.store(1, std::memory_order_release);
+  return SGEMM_OK;
+}
+
+int sgemm_destroy(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_refs == 0) return SGEMM_ERR_NOT_INITIALIZED;
+  if (--g_refs == 0) g_ready.store(0, std::memory_order_release);
+  return SGEMM_OK;
+}
+
+int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                      const float *B, int64_t ldb, float *C, int64_t ldc, void *stream) {
+  // Argument errors are reported before anything touches the runtime.
+  if (variant < 0 || variant >= SGEMM_NUM_VARIANTS) return SGEMM_ERR_INVALID_VALUE;
+  int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc);
+  if (rc != SGEMM_OK) return rc;
+  if (!g_ready.load(std::memory_order_acquire)) return SGEMM_ERR_NOT_INITIALIZED;
+  if (M == 0 || N == 0) return SGEMM_OK;
+  DeviceInfo di;
+  rc = current_device_info(&di);
+  if (rc != SGEMM_OK) return rc;
+
+  sgemm::GemmArgs p;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.A = A;
+  p.lda = lda;
+  p.B = B;
+  p.ldb = ldb;
+  p.C = C;
+  p.ldc = ldc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  hipError_t err;
+  if (K == 0) {
+    err = sgemm::launch_zero(p, s);
+  } else {
+    const bool va = aligned16(A) && lda % 4 == 0 && K % 4 == 0;
+    const bool vb = aligned16(B) && ldb % 4 == 0 && N % 4 == 0;
+    switch (variant) {
+      case SGEMM_VARIANT_NAIVE:
+      case SGEMM_VARIANT_LDS:
+      case SGEMM_VARIANT_REG:
+      case SGEMM_VARIANT_DBUF:
+        err = sgemm::launch_valu(variant - SGEMM_VARIANT_NAIVE, p, va, vb, s);
+        break;
+      case SGEMM_VARIANT_MFMA_256:
+        err = sgemm::launch_mfma(sgemm::MfmaTile::T256, p, va, vb, s);
+        break;
+      case SGEMM_VARIANT_MFMA_128:
+        err = sgemm::launch_mfma(sgemm::MfmaTile::T128, p, va, vb, s);
+        break;
+      case SGEMM_VARIANT_MFMA_64:
+        err = sgemm::launch_mfma(sgemm::MfmaTile::T64, p, va, vb, s);
+        break;
+      default:
+        err = sgemm::launch_mfma(choose_tile(M, N, di.cus), p, va, vb, s);
+        break;
+    }
+  }
+  return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+int sgemm_run(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+              int64_t ldb, float *C, int64_t ldc, void *stream) {
+  return sgemm_run_variant(SGEMM_VARIANT_MFMA, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int sgemm_mfma_probe(int which, const float *A, const float *B, float *C, void *stream) {
+  if ((which != 0 && which != 1) || !A || !B || !C) return SGEMM_ERR_INVALID_VALUE;
+  if (!g_ready.load(std::memory_order_acquire)) return SGEMM_ERR_NOT_INITIALIZED;
+  DeviceInfo di;
+  const int rc = current_device_info(&di);
+  if (rc != SGEMM_OK) return rc;
+  const hipError_t err =
+      sgemm::launch_mfma_probe(which, A, B, C, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+const char *sgemm_status_string(int status) {
+  switch (status) {
+    case SGEMM_OK: return "SGEMM_OK";
+    case SGEMM_ERR_INVALID_VALUE: return "SGEMM_ERR_INVALID_VALUE";
+    case SGEMM_ERR_NOT_INITIALIZED: return "SGEMM_ERR_NOT_INITIALIZED";
+    case SGEMM_ERR_UNSUPPORTED_DEVICE: return "SGEMM_ERR_UNSUPPORTED_DEVICE";
+    case SGEMM_ERR_HIP: return "SGEMM_ERR_HIP";
+    case SGEMM_ERR_LAUNCH: return "SGEMM_ERR_LAUNCH";
+    case SGEMM_ERR_TOO_LARGE: return "SGEMM_ERR_TOO_LARGE";
+    default: return "unknown status";
+  }
+}
+
+const char *sgemm_variant_name(int variant) {
+  switch (variant) {
+    case SGEMM_VARIANT_NAIVE: return "valu_naive";
+    case SGEMM_VARIANT_LDS: return "valu_lds_tiled";
+    case SGEMM_VARIANT_REG: return "valu_register_tiled";
+    case SGEMM_VARIANT_DBUF: return "valu_double_buffered";
+    case SGEMM_VARIANT_MFMA: return "mfma_auto";
+    case SGEMM_VARIANT_MFMA_256: return "mfma_256x256";
+    case SGEMM_VARIANT_MFMA_128: return "mfma_128x128";
+    case SGEMM_VARIANT_MFMA_64: return "mfma_64x64";
+    default: return nullptr;
+  }
+}
+
+}  // extern "C"

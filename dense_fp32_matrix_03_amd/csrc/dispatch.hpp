@@ -1,0 +1,27 @@
+// dispatch.hpp -- host-side launchers of the kernels (C++ linkage, internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace sgemm {
+
+// Block tiles of the matrix-core kernel.
+enum class MfmaTile { T256, T128, T64 };
+
+// Matrix-core product.  va / vb: A / B qualify for 128-bit loads.
+hipError_t launch_mfma(MfmaTile tile, const GemmArgs &p, bool va, bool vb, hipStream_t stream);
+
+// One-instruction lane-layout probe (which: 0 = 32x32x2, 1 = 16x16x4).
+hipError_t launch_mfma_probe(int which, const float *A, const float *B, float *C,
+                             hipStream_t stream);
+
+// Vector-FMA progression: 0 naive, 1 LDS-tiled, 2 register-tiled,
+// 3 register-tiled with a double-buffered LDS pipeline.
+hipError_t launch_valu(int rung, const GemmArgs &p, bool va, bool vb, hipStream_t stream);
+
+// C[0:M, 0:N] = 0 (the K == 0 product).
+hipError_t launch_zero(const GemmArgs &p, hipStream_t stream);
+
+}  // namespace sgemm

@@ -1,0 +1,213 @@
+// valu_kernels.hip -- the pages' progression on the vector FMA units, kept as
+// the ablation ladder beside the matrix-core kernel:
+//   rung 0  one thread per output, operands straight from global memory
+//           (blog "【infra之路】03_动手写 CUDA Kernel", v1 Naive; article
+//           "硬件加速原理：CUDA核函数优化矩阵乘法的内存访问模式", basic kernel);
+//   rung 1  32 x 32 LDS tiles, one output per thread, zero-filled edges
+//           (blog v2 Shared Memory Tiled; textbook chapter "4. 矩阵乘法性能
+//           优化", section 三);
+//   rung 2  128 x 128 x 16 block tiles, 256 threads, 8 x 8 outputs per thread
+//           as an outer product of 8 A and 8 B register values (chapter
+//           sections 一 and 二);
+//   rung 3  rung 2 with two LDS stages: slice t+1 is fetched while slice t is
+//           computed (chapter section 四).
+// All rungs run every product; none uses packed FMA.
+#include "common.hpp"
+#include "dispatch.hpp"
+
+namespace sgemm {
+
+// ---------------------------------------------------------------- rung 0
+__global__ void __launch_bounds__(256) naive_kernel(GemmArgs p, int tiles_n) {
+  const int bx = blockIdx.x % tiles_n, by = blockIdx.x / tiles_n;
+  const int col = bx * 16 + (threadIdx.x % 16);
+  const int row = by * 16 + (threadIdx.x / 16);
+  if (row >= p.M || col >= p.N) return;
+  const float *a = p.A + (long)row * p.lda;
+  const float *b = p.B + col;
+  float sum = 0.f;
+  for (int k = 0; k < p.K; ++k) sum = fmaf(a[k], b[(long)k * p.ldb], sum);
+  p.C[(long)row * p.ldc + col] = sum;
+}
+
+// ---------------------------------------------------------------- rung 1
+constexpr int kTile = 32;
+
+__global__ void __launch_bounds__(kTile *kTile) lds_tiled_kernel(GemmArgs p, int tiles_n) {
+  __shared__ float sA[kTile][kTile];
+  __shared__ float sB[kTile][kTile];
+  const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;
+  const int bx = blockIdx.x % tiles_n, by = blockIdx.x / tiles_n;
+  const int row = by * kTile + ty, col = bx * kTile + tx;
+  float sum = 0.f;
+  for (int k0 = 0; k0 < p.K; k0 += kTile) {
+    sA[ty][tx] = (row < p.M && k0 + tx < p.K) ? p.A[(long)row * p.lda + k0 + tx] : 0.f;
+    sB[ty][tx] = (k0 + ty < p.K && col < p.N) ? p.B[(long)(k0 + ty) * p.ldb + col] : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kTile; ++k) sum = fmaf(sA[ty][k], sB[k][tx], sum);
+    __syncthreads();
+  }
+  if (row < p.M && col < p.N) p.C[(long)row * p.ldc + col] = sum;
+}
+
+// ---------------------------------------------------------------- rungs 2, 3
+// Thread (tx, ty) = (tid % 16, tid / 16) owns rows {4ty + i, 64 + 4ty + i}
+// and columns {4tx + j, 64 + 4tx + j}, i, j < 4: its 8 x 8 outputs as four
+// 4 x 4 quadrants.  A is stored transposed in LDS (k-major), so both operand
+// vectors are contiguous 128-bit LDS reads, and the 16 threads of a row of
+// the thread grid read 16 consecutive 16-byte chunks of B (no bank
+// conflicts, where the chapter pads a k-minor A instead).
+constexpr int kRB = 128, kRK = 16, kRT = 256;
+
+template <bool DBUF, bool VA, bool VB>
+__global__ void __launch_bounds__(kRT) regtile_kernel(GemmArgs p, int tiles_n) {
+  constexpr int NS = DBUF ? 2 : 1;
+  constexpr int SAT = kRB + 4;  // LDS row stride of transposed A (k rows)
+  using FetchA = SliceFetch<kRB, kRK, kRT, VA>;
+  using FetchB = SliceFetch<kRK, kRB, kRT, VB>;
+  __shared__ __attribute__((aligned(16))) float sAt[NS][kRK * SAT];
+  __shared__ __attribute__((aligned(16))) float sB[NS][kRK * kRB];
+
+  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+  const int bx = blockIdx.x % tiles_n, by = blockIdx.x / tiles_n;
+  const int m0 = by * kRB, n0 = bx * kRB;
+
+  FetchA fa;
+  FetchB fb;
+  fa.init(p.A, p.lda, m0, 0, tid);
+  fb.init(p.B, p.ldb, 0, n0, tid);
+
+  auto store_slice = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < FetchA::CH; ++i) {
+      const int r = FetchA::wrow(tid, i), c = FetchA::wcol(tid);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sAt[s][(c + e) * SAT + r] = fa.v[i][e];
+    }
+#pragma unroll
+    for (int i = 0; i < FetchB::CH; ++i)
+      *reinterpret_cast<f32x4 *>(&sB[s][FetchB::wrow(tid, i) * kRB + FetchB::wcol(tid)]) =
+          fb.v[i];
+  };
+
+  float acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+
+  auto compute_slice = [&](int s) {
+#pragma unroll
+    for (int k = 0; k < kRK; ++k) {
+      const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&sAt[s][k * SAT + 4 * ty]);
+      const f32x4 a1 = *reinterpret_cast<const f32x4 *>(&sAt[s][k * SAT + 64 + 4 * ty]);
+      const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&sB[s][k * kRB + 4 * tx]);
+      const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&sB[s][k * kRB + 64 + 4 * tx]);
+      float a[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      float b[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+  };
+
+  const int nk = (p.K + kRK - 1) / kRK;
+  if constexpr (!DBUF) {
+    // load -> barrier -> compute -> barrier, as in the pages' tiled kernels.
+    for (int t = 0; t < nk; ++t) {
+      fa.load(p.M, p.K);
+      fb.load(p.K, p.N);
+      store_slice(0);
+      __syncthreads();
+      compute_slice(0);
+      __syncthreads();
+      fa.advance(0, kRK);
+      fb.advance(kRK, 0);
+    }
+  } else {
+    fa.load(p.M, p.K);
+    fb.load(p.K, p.N);
+    store_slice(0);
+    __syncthreads();
+    for (int t = 0; t < nk; ++t) {
+      const bool more = t + 1 < nk;
+      if (more) {
+        fa.advance(0, kRK);
+        fb.advance(kRK, 0);
+        fa.load(p.M, p.K);
+        fb.load(p.K, p.N);
+      }
+      compute_slice(t & 1);
+      if (more) store_slice((t + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = m0 + (i < 4 ? 4 * ty + i : 64 + 4 * ty + i - 4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int col = n0 + (j < 4 ? 4 * tx + j : 64 + 4 * tx + j - 4);
+      if (row < p.M && col < p.N) p.C[(long)row * p.ldc + col] = acc[i][j];
+    }
+  }
+}
+
+template <bool DBUF>
+static void launch_regtile(const GemmArgs &p, bool va, bool vb, hipStream_t stream) {
+  const int tiles_n = (p.N + kRB - 1) / kRB, tiles_m = (p.M + kRB - 1) / kRB;
+  const dim3 grid((unsigned)((long)tiles_m * tiles_n)), block(kRT);
+  if (va && vb)
+    hipLaunchKernelGGL((regtile_kernel<DBUF, true, true>), grid, block, 0, stream, p, tiles_n);
+  else if (va)
+    hipLaunchKernelGGL((regtile_kernel<DBUF, true, false>), grid, block, 0, stream, p, tiles_n);
+  else if (vb)
+    hipLaunchKernelGGL((regtile_kernel<DBUF, false, true>), grid, block, 0, stream, p, tiles_n);
+  else
+    hipLaunchKernelGGL((regtile_kernel<DBUF, false, false>), grid, block, 0, stream, p, tiles_n);
+}
+
+hipError_t launch_valu(int rung, const GemmArgs &p, bool va, bool vb, hipStream_t stream) {
+  switch (rung) {
+    case 0: {
+      const int tiles_n = (p.N + 15) / 16, tiles_m = (p.M + 15) / 16;
+      hipLaunchKernelGGL(naive_kernel, dim3((unsigned)((long)tiles_m * tiles_n)), dim3(256), 0,
+                         stream, p, tiles_n);
+      break;
+    }
+    case 1: {
+      const int tiles_n = (p.N + kTile - 1) / kTile, tiles_m = (p.M + kTile - 1) / kTile;
+      hipLaunchKernelGGL(lds_tiled_kernel, dim3((unsigned)((long)tiles_m * tiles_n)),
+                         dim3(kTile * kTile), 0, stream, p, tiles_n);
+      break;
+    }
+    case 2: launch_regtile<false>(p, va, vb, stream); break;
+    case 3: launch_regtile<true>(p, va, vb, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- K == 0
+__global__ void __launch_bounds__(256) zero_kernel(float *C, long ldc, int M, int N) {
+  const long total = (long)M * N;
+  for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+       q += (long)gridDim.x * blockDim.x) {
+    const long row = q / N, col = q % N;
+    C[row * ldc + col] = 0.f;
+  }
+}
+
+hipError_t launch_zero(const GemmArgs &p, hipStream_t stream) {
+  const long total = (long)p.M * p.N;
+  long blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p.C, p.ldc, p.M,
+                     p.N);
+  return hipGetLastError();
+}
+
+}  // namespace sgemm

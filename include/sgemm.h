@@ -1,0 +1,137 @@
+/*
+ * sgemm.h -- C interface of libsgemm, a single-precision matrix product for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  C = A x B for row-major single-precision matrices, where A
+ * is M x K, B is K x N and C is M x N, and entry (i, j) of C is the sum over
+ * k of A(i,k) * B(k,j).  Definition: article "硬件加速原理：CUDA核函数优化矩阵
+ * 乘法的内存访问模式", section "矩阵乘法的计算特性" (the summation formula), and
+ * the opening paragraph of the textbook chapter "4. 矩阵乘法性能优化".  The
+ * pages' kernels overwrite C with the sum and never read it; so does this
+ * library: there is no alpha or beta.
+ *
+ * Layout.  Element (i, k) of A is A[i*lda + k]; element (k, j) of B is
+ * B[k*ldb + j]; element (i, j) of C is C[i*ldc + j] (the row-major indexing
+ * of the blog "【infra之路】03_动手写 CUDA Kernel", v1 Naive, generalised to
+ * leading dimensions).  Requirements: lda >= max(1, K), ldb >= max(1, N),
+ * ldc >= max(1, N).  Columns j in [N, ldc) of C are never written; columns
+ * beyond K of A and beyond N of B are never read into the result.
+ *
+ * Numerics.  Products and sums are single precision with fused multiply-add
+ * (the matrix cores fuse); the order of summation is fixed for a given call
+ * shape, so repeated calls give identical bits.  The accuracy contract is
+ * |C(i,j) - exact| <= 1e-5 * sum_k |A(i,k) B(k,j)| + 1e-6 for finite inputs.
+ * NaN or infinite inputs are outside the contract.
+ *
+ * Pointers and ownership.  A, B and C are device pointers owned by the
+ * caller; the library allocates no memory per call and keeps no pointer
+ * after a call returns.  C must not overlap A or B.  Any 4-byte alignment is
+ * accepted; 16-byte alignment with leading dimensions and widths that are
+ * multiples of 4 enables 128-bit loads.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ * stream of the current device).  Calls are asynchronous: they return once
+ * the work is enqueued on the current device; a fault in the kernel shows up
+ * at the caller's next synchronisation with that stream.
+ *
+ * Errors.  Every call returns SGEMM_OK (0) or a negative status; nothing is
+ * enqueued when a status other than SGEMM_OK is returned, except
+ * SGEMM_ERR_LAUNCH, which reports that the runtime rejected a launch.
+ * Argument errors (SGEMM_ERR_INVALID_VALUE, SGEMM_ERR_TOO_LARGE) are found
+ * before the library or the HIP runtime is consulted, so they are reported
+ * even before sgemm_create.  sgemm_status_string() names each status.
+ *
+ * Threads.  sgemm_create / sgemm_destroy are serialised internally;
+ * sgemm_run may be called from any thread once sgemm_create has succeeded.
+ */
+#ifndef SGEMM_H_
+#define SGEMM_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGEMM_OK 0
+#define SGEMM_ERR_INVALID_VALUE (-1)    /* negative size, short ld, null pointer, bad variant */
+#define SGEMM_ERR_NOT_INITIALIZED (-2)  /* sgemm_run before sgemm_create */
+#define SGEMM_ERR_UNSUPPORTED_DEVICE (-3) /* current device is not gfx950 */
+#define SGEMM_ERR_HIP (-4)              /* a HIP runtime query failed */
+#define SGEMM_ERR_LAUNCH (-5)           /* the runtime rejected a kernel launch */
+#define SGEMM_ERR_TOO_LARGE (-6)        /* a dimension is 2^31 or more */
+
+/*
+ * Kernel variants for sgemm_run_variant.  The first four are the pages'
+ * progression on vector FMA units -- one thread per output (blog v1 Naive;
+ * article "基础矩陣乘法"), LDS tiling (blog v2 Shared Memory Tiled; chapter
+ * section 三), register tiling with 8x8 outputs per thread over 128x128x16
+ * blocks (chapter sections 一 and 二), and that with a double-buffered LDS
+ * pipeline (chapter section 四).  SGEMM_VARIANT_MFMA is the matrix-core
+ * path that sgemm_run uses; the _MFMA_<n> variants force its n x n block
+ * tile instead of choosing one from the shape.
+ */
+#define SGEMM_VARIANT_NAIVE 0
+#define SGEMM_VARIANT_LDS 1
+#define SGEMM_VARIANT_REG 2
+#define SGEMM_VARIANT_DBUF 3
+#define SGEMM_VARIANT_MFMA 4
+#define SGEMM_VARIANT_MFMA_256 5
+#define SGEMM_VARIANT_MFMA_128 6
+#define SGEMM_VARIANT_MFMA_64 7
+#define SGEMM_NUM_VARIANTS 8
+
+/*
+ * Initialise the library for the current device: checks that it is gfx950
+ * and caches its compute-unit count.  Reference counted; each successful
+ * call must be matched by sgemm_destroy.  Returns SGEMM_OK,
+ * SGEMM_ERR_UNSUPPORTED_DEVICE or SGEMM_ERR_HIP.
+ */
+int sgemm_create(void);
+
+/* Drop one reference taken by sgemm_create.  SGEMM_ERR_NOT_INITIALIZED if none. */
+int sgemm_destroy(void);
+
+/*
+ * C = A x B on `stream` (see the layout and numerics above).  M == 0 or
+ * N == 0 is a successful no-op; K == 0 writes zeros to the M x N block of C
+ * (the empty sum).  A and B may be NULL when M*N*K == 0; C may be NULL when
+ * M*N == 0.
+ */
+int sgemm_run(int64_t M, int64_t N, int64_t K,
+              const float *A, int64_t lda,
+              const float *B, int64_t ldb,
+              float *C, int64_t ldc, void *stream);
+
+/*
+ * Same contract as sgemm_run, computed by kernel `variant`
+ * (SGEMM_VARIANT_*).  Every variant meets the same accuracy contract.
+ * SGEMM_ERR_INVALID_VALUE for an unknown variant.
+ */
+int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K,
+                      const float *A, int64_t lda,
+                      const float *B, int64_t ldb,
+                      float *C, int64_t ldc, void *stream);
+
+/*
+ * Matrix-core layout probe: one wave multiplies a 32 x 2 block of A by a
+ * 2 x 32 block of B (which = 0, v_mfma_f32_32x32x2_f32) or a 16 x 4 block by
+ * a 4 x 16 block (which = 1, v_mfma_f32_16x16x4_f32), with A and B row-major
+ * and packed, and writes the 32 x 32 (or 16 x 16) product row-major and
+ * packed to C.  It exercises the operand and accumulator lane maps that the
+ * matrix-core kernels rely on.  SGEMM_ERR_INVALID_VALUE for another `which`
+ * or a null pointer.
+ */
+int sgemm_mfma_probe(int which, const float *A, const float *B, float *C, void *stream);
+
+/* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
+const char *sgemm_status_string(int status);
+
+/* Static, NUL-terminated name of a variant, or NULL for an unknown one. */
+const char *sgemm_variant_name(int variant);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_H_ */

@@ -26,3 +26,13 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_test(request):
+    # Name each GPU test on the real stderr before it runs, so that a run that
+    # ends abruptly still shows which case was on the device.
+    if "gpu" in request.node.keywords:
+        sys.__stderr__.write(f"\n[gpu test] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

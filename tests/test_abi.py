@@ -1,0 +1,84 @@
+"""The C-ABI library loads on the host and exports what include/sgemm.h declares.
+
+These tests make no compute call: they need no GPU.  Host-only behaviour
+(status names, argument checks that precede any runtime call) is exercised
+through the same ctypes binding the GPU tests use.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_fp32_matrix_03_amd as sg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^[\w\s\*]*?\b(\w+)\s*\([^;{]*\)\s*;", text, flags=re.M)
+    return names
+
+
+def test_header_declares_the_entry_points():
+    names = set(_declared_functions())
+    for n in ("sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_run_variant",
+              "sgemm_mfma_probe", "sgemm_status_string", "sgemm_variant_name"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(sg.LIB_PATH)
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    for name, code in sg._C.items():
+        if name.startswith("SGEMM_ERR_") or name == "SGEMM_OK":
+            assert sg.sgemm_status_string(code) == name
+    assert sg.sgemm_status_string(12345) == "unknown status"
+
+
+def test_variant_names():
+    for key, v in sg.VARIANTS.items():
+        assert sg.sgemm_variant_name(v) is not None
+    assert sg.sgemm_variant_name(sg.NUM_VARIANTS) is None
+    assert sg.sgemm_variant_name(-1) is None
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 4, 4, 1, 4, 1, 4, 1, 4), "SGEMM_ERR_INVALID_VALUE"),   # negative M
+    ((4, 4, 4, 1, 3, 1, 4, 1, 4), "SGEMM_ERR_INVALID_VALUE"),    # lda < K
+    ((4, 4, 4, 1, 4, 1, 3, 1, 4), "SGEMM_ERR_INVALID_VALUE"),    # ldb < N
+    ((4, 4, 4, 1, 4, 1, 4, 1, 3), "SGEMM_ERR_INVALID_VALUE"),    # ldc < N
+    ((4, 4, 4, 0, 4, 1, 4, 1, 4), "SGEMM_ERR_INVALID_VALUE"),    # null A
+    ((4, 4, 4, 1, 4, 1, 4, 0, 4), "SGEMM_ERR_INVALID_VALUE"),    # null C
+    ((2 ** 31, 4, 4, 1, 4, 1, 4, 1, 4), "SGEMM_ERR_TOO_LARGE"),
+    ((4, 4, 4, 1, 4, 1, 4, 1, 4), "SGEMM_ERR_NOT_INITIALIZED"),  # valid, before create
+])
+def test_host_side_argument_checks(args, status):
+    lib = sg.load_library()
+    M, N, K, A, lda, B, ldb, C, ldc = args
+    rc = lib.sgemm_run(M, N, K, A or None, lda, B or None, ldb, C or None, ldc, None)
+    assert sg.sgemm_status_string(rc) == status
+    rc = lib.sgemm_run_variant(0, M, N, K, A or None, lda, B or None, ldb, C or None, ldc, None)
+    assert sg.sgemm_status_string(rc) == status
+
+
+def test_unknown_variant_rejected():
+    lib = sg.load_library()
+    rc = lib.sgemm_run_variant(sg.NUM_VARIANTS, 4, 4, 4, 1, 4, 1, 4, 1, 4, None)
+    assert sg.sgemm_status_string(rc) == "SGEMM_ERR_INVALID_VALUE"
+    rc = lib.sgemm_mfma_probe(2, 1, 1, 1, None)
+    assert sg.sgemm_status_string(rc) == "SGEMM_ERR_INVALID_VALUE"
+
+
+def test_destroy_without_create():
+    lib = sg.load_library()
+    assert sg.sgemm_status_string(lib.sgemm_destroy()) == "SGEMM_ERR_NOT_INITIALIZED"

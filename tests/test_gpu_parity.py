@@ -1,0 +1,281 @@
+"""Parity of the HIP path with the CPU oracle, through the C-ABI.
+
+Every product here is computed by libsgemm on the GPU and compared element by
+element with the double-precision oracle on the same seeded inputs:
+
+* the tolerance |C - Cref| <= 1e-5 * sum_k |A(i,k) B(k,j)| + 1e-6 with C
+  finite (C is pre-filled with NaN, so an entry never written fails);
+* bit-exact agreement for small-integer inputs, where single precision is
+  exact;
+* at 8192^3, 4096 sampled entries against the oracle plus whole-matrix checks
+  (every entry finite, a double-precision Freivalds check, and exact integer
+  Freivalds checks on an integer-valued product).
+"""
+import numpy as np
+import pytest
+
+import dense_fp32_matrix_03_amd as sg
+import oracle
+from dense_fp32_matrix_03_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+MFMA_VARIANTS = ["mfma", "mfma_256", "mfma_128", "mfma_64"]
+VALU_VARIANTS = ["naive", "lds", "reg", "dbuf"]
+ALL_VARIANTS = VALU_VARIANTS + MFMA_VARIANTS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def library():
+    sg.sgemm_create()
+    yield
+    sg.sgemm_destroy()
+
+
+def _dev(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _run(A, B, M, N, K, variant="mfma", ldc=None, lda=None, ldb=None):
+    """Run one product on the GPU from host arrays; return C (M x ldc) on the host."""
+    import torch
+    lda = A.shape[1] if lda is None else lda
+    ldb = B.shape[1] if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    dA, dB = _dev(A), _dev(B)
+    dC = torch.full((max(M, 1), ldc), float("nan"), dtype=torch.float32, device="cuda")
+    sg.sgemm_run_variant(variant, M, N, K, dA, lda, dB, ldb, dC, ldc)
+    torch.cuda.synchronize()
+    return dC.cpu().numpy()[:M]
+
+
+# -- layout probe ---------------------------------------------------------------
+
+@pytest.mark.parametrize("which,m,k", [(0, 32, 2), (1, 16, 4)])
+def test_mfma_probe_index_encoded(which, m, k):
+    """A(i,k) = i + 100 k, B(k,j) = 1000 k - j: integers, so exact."""
+    import torch
+    A = np.array([[i + 100 * kk for kk in range(k)] for i in range(m)], dtype=np.float32)
+    B = np.array([[1000 * kk - j for j in range(m)] for kk in range(k)], dtype=np.float32)
+    dC = torch.full((m, m), float("nan"), dtype=torch.float32, device="cuda")
+    sg.sgemm_mfma_probe(which, _dev(A), _dev(B), dC)
+    torch.cuda.synchronize()
+    Cref, _ = oracle.sgemm_f64(A, B)
+    assert np.array_equal(dC.cpu().numpy().astype(np.float64), Cref)
+
+
+# -- the five workloads -----------------------------------------------------------
+
+@pytest.mark.parametrize("w", inputs.WORKLOADS[:4], ids=lambda w: w.name)
+def test_workload_tolerance(w):
+    A, B = inputs.make_inputs(w)
+    C = _run(A, B, w.M, w.N, w.K, ldc=w.ldc)
+    Cref, Sabs = oracle.sgemm_f64(A, B, K=w.K, N=w.N)
+    r = oracle.check(C[:, :w.N], Cref, Sabs)
+    print(f"{w.name}: {r}")
+    assert r.ok, str(r)
+    assert r.usage < 0.05, f"tolerance usage {r.usage} suggests a precision defect"
+
+
+@pytest.mark.parametrize("w", inputs.WORKLOADS[:4], ids=lambda w: w.name)
+def test_workload_integer_exact(w):
+    A, B = inputs.make_inputs(w, dist="int8range")
+    C = _run(A, B, w.M, w.N, w.K, ldc=w.ldc)
+    Cref, _ = oracle.sgemm_f64(A, B, K=w.K, N=w.N)
+    assert np.array_equal(C[:, :w.N].astype(np.float64), Cref)
+
+
+def _big():
+    return inputs.WORKLOADS[4]
+
+
+def test_8192_sampled_and_whole_matrix():
+    import torch
+    w = _big()
+    A, B = inputs.make_inputs(w)
+    C = _run(A, B, w.M, w.N, w.K)
+    assert np.all(np.isfinite(C)), "an output entry was never written"
+    I, J = inputs.sample_indices(w.M, w.N, w.seed)
+    cref, sabs = oracle.entries_f64(A, B, I, J)
+    r = oracle.check(C[I, J], cref, sabs)
+    print(f"{w.name} sampled: {r}")
+    assert r.ok, str(r)
+    assert r.usage < 0.05
+    ok, usage = oracle.freivalds(A, B, C, inputs.sign_vector(w.N, w.seed))
+    print(f"{w.name} freivalds usage {usage:.3e}")
+    assert ok
+    del C
+    torch.cuda.empty_cache()
+
+
+def test_8192_integer_exact_whole_matrix():
+    """Integer inputs in [-8, 8]: every partial sum is below 2^24, so C is exact
+    and (C x) == A (B x) holds exactly in int64 for integer probe vectors."""
+    w = _big()
+    A, B = inputs.make_inputs(w, dist="int8range")
+    C = _run(A, B, w.M, w.N, w.K)
+    assert np.all(np.isfinite(C))
+    Ci = C.astype(np.int64)
+    assert np.array_equal(Ci.astype(np.float32), C)
+    Ai, Bi = A.astype(np.int64), B.astype(np.int64)
+    g = np.random.default_rng(99)
+    for _ in range(3):
+        x = g.integers(-1000, 1001, size=w.N, dtype=np.int64)
+        assert np.array_equal(Ci @ x, Ai @ (Bi @ x))
+    I, J = inputs.sample_indices(w.M, w.N, w.seed)
+    cref, _ = oracle.entries_f64(A, B, I, J)
+    assert np.array_equal(C[I, J].astype(np.float64), cref)
+
+
+def test_8192_rank1_closed_form():
+    """A(i,k) = u_i, B(k,j) = v_j: C(i,j) = K u_i v_j exactly, no oracle needed."""
+    w = _big()
+    g = np.random.default_rng(4)
+    u = inputs.small_integers(g, (w.M,))
+    v = inputs.small_integers(g, (w.N,))
+    A = np.repeat(u[:, None], w.K, axis=1)
+    B = np.repeat(v[None, :], w.K, axis=0)
+    C = _run(A, B, w.M, w.N, w.K)
+    expect = (w.K * np.outer(u.astype(np.int64), v.astype(np.int64))).astype(np.float32)
+    assert np.array_equal(C, expect)
+
+
+# -- every variant ------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant", ALL_VARIANTS)
+@pytest.mark.parametrize("w", [inputs.WORKLOADS[0], inputs.WORKLOADS[3]], ids=lambda w: w.name)
+def test_variant_tolerance(variant, w):
+    A, B = inputs.make_inputs(w)
+    C = _run(A, B, w.M, w.N, w.K, variant=variant, ldc=w.ldc)
+    Cref, Sabs = oracle.sgemm_f64(A, B, K=w.K, N=w.N)
+    r = oracle.check(C[:, :w.N], Cref, Sabs)
+    assert r.ok, f"{variant}: {r}"
+    assert r.usage < 0.05
+
+
+@pytest.mark.parametrize("variant", ALL_VARIANTS)
+def test_variant_integer_exact_1024(variant):
+    w = inputs.WORKLOADS[1]
+    A, B = inputs.make_inputs(w, dist="int8range")
+    C = _run(A, B, w.M, w.N, w.K, variant=variant)
+    Cref, _ = oracle.sgemm_f64(A, B)
+    assert np.array_equal(C.astype(np.float64), Cref)
+
+
+# -- edges: ragged shapes, padding, alignment ------------------------------------------
+
+EDGE_DIMS = [1, 2, 3, 5, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+def _edge_shapes(n, seed):
+    g = np.random.default_rng(seed)
+    return [tuple(int(x) for x in g.choice(EDGE_DIMS, 3)) for _ in range(n)]
+
+
+@pytest.mark.parametrize("variant", ALL_VARIANTS)
+def test_edge_shape_sweep(variant):
+    for (M, N, K) in _edge_shapes(24, 7 + ALL_VARIANTS.index(variant)) + [(1, 1, 1), (257, 255, 3)]:
+        g = np.random.default_rng(M * 65536 + N * 256 + K)
+        A = inputs.uniform(g, (M, K))
+        B = inputs.uniform(g, (K, N))
+        C = _run(A, B, M, N, K, variant=variant)
+        Cref, Sabs = oracle.sgemm_f64(A, B)
+        r = oracle.check(C, Cref, Sabs)
+        assert r.ok, f"{variant} M={M} N={N} K={K}: {r}"
+
+
+@pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "reg", "dbuf"])
+def test_padded_leading_dimensions(variant):
+    """NaN in the padding of A and B must not reach C; C's padding is untouched."""
+    M, N, K = 200, 136, 72
+    g = np.random.default_rng(31)
+    A = inputs.padded(inputs.uniform(g, (M, K)), K + 12)
+    B = inputs.padded(inputs.uniform(g, (K, N)), N + 8)
+    C = _run(A, B, M, N, K, variant=variant, ldc=N + 20)
+    Cref, Sabs = oracle.sgemm_f64(A, B, K=K, N=N)
+    r = oracle.check(C[:, :N], Cref, Sabs)
+    assert r.ok, str(r)
+    assert np.all(np.isnan(C[:, N:])), "C padding columns were written"
+
+
+@pytest.mark.parametrize("variant", ["mfma", "mfma_128", "dbuf"])
+def test_misaligned_pointers(variant):
+    """Operands that start 4 bytes past a 16-byte boundary take the 32-bit path."""
+    import torch
+    M, N, K = 130, 100, 68
+    g = np.random.default_rng(37)
+    A = inputs.uniform(g, (M, K))
+    B = inputs.uniform(g, (K, N))
+    bufA = _dev(np.concatenate([np.zeros(1, np.float32), A.ravel()]))
+    bufB = _dev(np.concatenate([np.zeros(3, np.float32), B.ravel()]))
+    dC = torch.full((M * N + 1,), float("nan"), dtype=torch.float32, device="cuda")
+    sg.sgemm_run_variant(variant, M, N, K, bufA.data_ptr() + 4, K, bufB.data_ptr() + 12, N,
+                         dC.data_ptr() + 4, N)
+    torch.cuda.synchronize()
+    C = dC.cpu().numpy()[1:].reshape(M, N)
+    Cref, Sabs = oracle.sgemm_f64(A, B)
+    r = oracle.check(C, Cref, Sabs)
+    assert r.ok, str(r)
+
+
+def test_identity_gives_A_exactly():
+    M, K = 300, 260
+    g = np.random.default_rng(41)
+    A = inputs.normal(g, (M, K))
+    C = _run(A, np.eye(K, dtype=np.float32), M, K, K)
+    assert np.array_equal(C, A)
+
+
+def test_deterministic_bits():
+    w = inputs.WORKLOADS[3]
+    A, B = inputs.make_inputs(w)
+    C1 = _run(A, B, w.M, w.N, w.K, ldc=w.ldc)
+    C2 = _run(A, B, w.M, w.N, w.K, ldc=w.ldc)
+    assert C1.tobytes() == C2.tobytes()
+
+
+# -- degenerate sizes and errors --------------------------------------------------------
+
+def test_k_zero_writes_zeros():
+    import torch
+    dC = torch.full((5, 7), float("nan"), dtype=torch.float32, device="cuda")
+    sg.sgemm_run(5, 6, 0, None, 1, None, 6, dC, 7)
+    torch.cuda.synchronize()
+    C = dC.cpu().numpy()
+    assert np.array_equal(C[:, :6], np.zeros((5, 6), np.float32))
+    assert np.all(np.isnan(C[:, 6]))
+
+
+def test_m_or_n_zero_is_a_noop():
+    import torch
+    dC = torch.full((4, 4), float("nan"), dtype=torch.float32, device="cuda")
+    sg.sgemm_run(0, 4, 4, None, 4, None, 4, dC, 4)
+    sg.sgemm_run(4, 0, 4, None, 4, None, 1, dC, 4)
+    torch.cuda.synchronize()
+    assert np.all(np.isnan(dC.cpu().numpy()))
+
+
+def test_errors_are_reported():
+    import torch
+    d = torch.zeros(16, device="cuda")
+    with pytest.raises(sg.SgemmError) as e:
+        sg.sgemm_run(4, 4, 4, d, 3, d, 4, d, 4)
+    assert e.value.status == sg._C["SGEMM_ERR_INVALID_VALUE"]
+    with pytest.raises(sg.SgemmError):
+        sg.sgemm_run_variant(99, 4, 4, 4, d, 4, d, 4, d, 4)
+
+
+def test_matmul_helper_and_streams():
+    import torch
+    g = np.random.default_rng(43)
+    A = inputs.uniform(g, (96, 80))
+    B = inputs.uniform(g, (80, 112))
+    s = torch.cuda.Stream()
+    dA, dB = _dev(A), _dev(B)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        dC = sg.matmul(dA, dB)
+    s.synchronize()
+    Cref, Sabs = oracle.sgemm_f64(A, B)
+    assert oracle.check(dC.cpu().numpy(), Cref, Sabs).ok
