@@ -7,7 +7,8 @@ One step is one call of sgemm_run on the 8192^3 workload (uniform[-1, 1)
 inputs from seed 4, already resident in HBM).  W untimed calls, then exactly
 K calls between two synchronisations, timed with HIP events recorded on the
 stream the kernels run on.  Prints one JSON line.  The 2048^3 workload is
-timed the same way and reported under "secondary".
+timed the same way (200 calls, after 0.3 s of untimed calls so that the
+clocks have settled) and reported under "secondary".
 
 The CPU baseline is the oracle (double-precision triple loop) timed on the
 host cores on a bounded sample of the same workload: the first R rows of C,
@@ -31,6 +32,7 @@ PEAK_TFLOPS = 157.3    # MI355X dense FP32 matrix-core peak (published)
 HEADLINE = "sgemm_8192x8192x8192_uniform_seed4"
 SECONDARY = "sgemm_2048x2048x2048_uniform_seed2"
 COUNTERS = os.path.join(ROOT, "profiles", "mfma_gemm_8192_hbm_counters.json")
+COPY_BYTES = 256 << 20  # bytes read (and written) by the copy-calibration kernel
 
 
 def kernel_source_digest() -> str:
@@ -57,7 +59,7 @@ def measured_traffic(workload: str):
     return c.get("hbm_bytes_per_launch")
 
 
-def time_gpu(w, variant: str, steps: int, warmup: int):
+def time_gpu(w, variant: str, steps: int, warmup: int, warm_seconds: float = 0.0):
     import torch
 
     import dense_fp32_matrix_03_amd as sg
@@ -77,6 +79,13 @@ def time_gpu(w, variant: str, steps: int, warmup: int):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # Optionally keep the device busy a little longer before timing, so that
+    # short kernels are not timed while the clocks are still ramping up.
+    t_end = time.perf_counter() + warm_seconds
+    while time.perf_counter() < t_end:
+        for _ in range(50):
+            step()
+        torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
@@ -118,12 +127,15 @@ def cpu_baseline(w, target_s: float = 12.0):
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description="single-precision GEMM throughput on MI355X")
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--variant", default="mfma", help="kernel variant (default: sgemm_run's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy three times (the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     a = ap.parse_args(argv)
 
     if a.gpus != 1:
@@ -141,6 +153,15 @@ def main(argv=None) -> int:
         print("no GPU visible", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if a.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": 3}), flush=True)
+        return 0
     sg.sgemm_create()
     w = inputs.BY_NAME[a.workload]
     variant = sg.VARIANTS[a.variant] if a.variant in sg.VARIANTS else int(a.variant)
@@ -164,7 +185,7 @@ def main(argv=None) -> int:
                        "traffic": traffic}
     if not a.no_secondary and w.name != SECONDARY:
         w2 = inputs.BY_NAME[SECONDARY]
-        ms2, finite2 = time_gpu(w2, variant, max(a.steps, 50), max(a.warmup, 10))
+        ms2, finite2 = time_gpu(w2, variant, 200, a.warmup, warm_seconds=0.3)
         t2 = w2.flops / (ms2 * 1e-3) / 1e12
         out["secondary"] = {"workload": w2.name, "value": round(t2, 3), "unit": "TFLOP/s",
                             "ms_per_step": round(ms2, 5),

@@ -65,15 +65,6 @@ int check_args(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, con
 
 inline bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-// Matrix-core block tile for a shape: the largest tile that still gives at
-// least one work-group per compute unit, else the smallest.
-sgemm::MfmaTile choose_tile(int64_t M, int64_t N, int cus) {
-  auto tiles = [&](int64_t t) { return ((M + t - 1) / t) * ((N + t - 1) / t); };
-  if (tiles(256) >= cus) return sgemm::MfmaTile::T256;
-  if (tiles(128) >= cus) return sgemm::MfmaTile::T128;
-  return sgemm::MfmaTile::T64;
-}
-
 }  // namespace
 
 extern "C" {
@@ -125,6 +116,9 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
   } else {
     const bool va = aligned16(A) && lda % 4 == 0 && K % 4 == 0;
     const bool vb = aligned16(B) && ldb % 4 == 0 && N % 4 == 0;
+    using sgemm::MfmaPath;
+    using sgemm::MfmaTile;
+    const MfmaTile autotile = sgemm::choose_mfma_tile(M, N, di.cus);
     switch (variant) {
       case SGEMM_VARIANT_NAIVE:
       case SGEMM_VARIANT_LDS:
@@ -133,16 +127,22 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
         err = sgemm::launch_valu(variant - SGEMM_VARIANT_NAIVE, p, va, vb, s);
         break;
       case SGEMM_VARIANT_MFMA_256:
-        err = sgemm::launch_mfma(sgemm::MfmaTile::T256, p, va, vb, s);
+        err = sgemm::launch_mfma(MfmaTile::T256, MfmaPath::Auto, p, va, vb, s);
         break;
       case SGEMM_VARIANT_MFMA_128:
-        err = sgemm::launch_mfma(sgemm::MfmaTile::T128, p, va, vb, s);
+        err = sgemm::launch_mfma(MfmaTile::T128, MfmaPath::Auto, p, va, vb, s);
         break;
       case SGEMM_VARIANT_MFMA_64:
-        err = sgemm::launch_mfma(sgemm::MfmaTile::T64, p, va, vb, s);
+        err = sgemm::launch_mfma(MfmaTile::T64, MfmaPath::Auto, p, va, vb, s);
+        break;
+      case SGEMM_VARIANT_MFMA_STAGED:
+        err = sgemm::launch_mfma(autotile, MfmaPath::Staged, p, va, vb, s);
+        break;
+      case SGEMM_VARIANT_MFMA_UNPADDED:
+        err = sgemm::launch_mfma(autotile, MfmaPath::Unpadded, p, va, vb, s);
         break;
       default:
-        err = sgemm::launch_mfma(choose_tile(M, N, di.cus), p, va, vb, s);
+        err = sgemm::launch_mfma(autotile, MfmaPath::Auto, p, va, vb, s);
         break;
     }
   }
@@ -188,6 +188,8 @@ const char *sgemm_variant_name(int variant) {
     case SGEMM_VARIANT_MFMA_256: return "mfma_256x256";
     case SGEMM_VARIANT_MFMA_128: return "mfma_128x128";
     case SGEMM_VARIANT_MFMA_64: return "mfma_64x64";
+    case SGEMM_VARIANT_MFMA_STAGED: return "mfma_register_staged";
+    case SGEMM_VARIANT_MFMA_UNPADDED: return "mfma_unpadded_lds";
     default: return nullptr;
   }
 }

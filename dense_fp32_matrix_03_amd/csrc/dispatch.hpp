@@ -7,11 +7,25 @@
 
 namespace sgemm {
 
-// Block tiles of the matrix-core kernel.
+// Block tiles of the matrix-core kernels.
 enum class MfmaTile { T256, T128, T64 };
 
+// Which matrix-core kernel:
+//  Auto      buffer-to-LDS loads when the operands allow them (16-byte
+//            aligned, ld % 4 == 0, K % 4 == 0, N % 4 == 0), else register
+//            staged;
+//  Staged    register-staged loads always;
+//  Unpadded  as Auto but without the LDS anti-conflict layout (no A swizzle,
+//            no A row padding), to measure what that layout buys.
+enum class MfmaPath { Auto, Staged, Unpadded };
+
+// Largest tile that still gives at least one work-group per compute unit,
+// else the smallest.
+MfmaTile choose_mfma_tile(long M, long N, int cus);
+
 // Matrix-core product.  va / vb: A / B qualify for 128-bit loads.
-hipError_t launch_mfma(MfmaTile tile, const GemmArgs &p, bool va, bool vb, hipStream_t stream);
+hipError_t launch_mfma(MfmaTile tile, MfmaPath path, const GemmArgs &p, bool va, bool vb,
+                       hipStream_t stream);
 
 // One-instruction lane-layout probe (which: 0 = 32x32x2, 1 = 16x16x4).
 hipError_t launch_mfma_probe(int which, const float *A, const float *B, float *C,

@@ -68,8 +68,13 @@ extern "C" {
  * section 三), register tiling with 8x8 outputs per thread over 128x128x16
  * blocks (chapter sections 一 and 二), and that with a double-buffered LDS
  * pipeline (chapter section 四).  SGEMM_VARIANT_MFMA is the matrix-core
- * path that sgemm_run uses; the _MFMA_<n> variants force its n x n block
- * tile instead of choosing one from the shape.
+ * path that sgemm_run uses: 16-byte aligned operands with leading
+ * dimensions, K and N multiples of 4 are fetched by buffer-to-LDS loads,
+ * others through registers.  The _MFMA_<n> variants force its n x n block
+ * tile instead of choosing one from the shape.  SGEMM_VARIANT_MFMA_STAGED
+ * always fetches through registers, and SGEMM_VARIANT_MFMA_UNPADDED drops
+ * the LDS anti-conflict layout (the chapter's padding, section 三): both
+ * exist to measure what those steps are worth.
  */
 #define SGEMM_VARIANT_NAIVE 0
 #define SGEMM_VARIANT_LDS 1
@@ -79,7 +84,9 @@ extern "C" {
 #define SGEMM_VARIANT_MFMA_256 5
 #define SGEMM_VARIANT_MFMA_128 6
 #define SGEMM_VARIANT_MFMA_64 7
-#define SGEMM_NUM_VARIANTS 8
+#define SGEMM_VARIANT_MFMA_STAGED 8
+#define SGEMM_VARIANT_MFMA_UNPADDED 9
+#define SGEMM_NUM_VARIANTS 10
 
 /*
  * Initialise the library for the current device: checks that it is gfx950

@@ -20,7 +20,7 @@ from dense_fp32_matrix_03_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
-MFMA_VARIANTS = ["mfma", "mfma_256", "mfma_128", "mfma_64"]
+MFMA_VARIANTS = ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_staged", "mfma_unpadded"]
 VALU_VARIANTS = ["naive", "lds", "reg", "dbuf"]
 ALL_VARIANTS = VALU_VARIANTS + MFMA_VARIANTS
 
@@ -185,11 +185,50 @@ def test_edge_shape_sweep(variant):
         assert r.ok, f"{variant} M={M} N={N} K={K}: {r}"
 
 
-@pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "reg", "dbuf"])
+# Dimensions that are multiples of 4 (so the buffer-to-LDS path is taken) but
+# of no tile size: ragged M/N tiles and a ragged last K slice.
+DMA_DIMS = [4, 8, 12, 28, 36, 60, 68, 124, 132, 252, 260, 516]
+
+
+@pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_unpadded"])
+def test_buffer_to_lds_edge_sweep(variant):
+    g0 = np.random.default_rng(53 + MFMA_VARIANTS.index(variant))
+    shapes = [tuple(int(x) for x in g0.choice(DMA_DIMS, 3)) for _ in range(20)]
+    for (M, N, K) in shapes + [(4, 4, 4), (516, 260, 36)]:
+        g = np.random.default_rng(M * 65536 + N * 256 + K)
+        A = inputs.uniform(g, (M, K))
+        B = inputs.uniform(g, (K, N))
+        C = _run(A, B, M, N, K, variant=variant)
+        Cref, Sabs = oracle.sgemm_f64(A, B)
+        r = oracle.check(C, Cref, Sabs)
+        assert r.ok, f"{variant} M={M} N={N} K={K}: {r}"
+
+
+@pytest.mark.parametrize("w,tile", [(inputs.WORKLOADS[1], "mfma_64"),
+                                    (inputs.WORKLOADS[2], "mfma_128")],
+                         ids=["1024", "2048"])
+def test_load_paths_agree_bitwise(w, tile):
+    """Buffer-to-LDS and register-staged fetches, with or without the LDS
+    anti-conflict layout, feed the same matrix-core sequence: at the tile
+    the shape selects they must give identical bits."""
+    import torch
+    A, B = inputs.make_inputs(w)
+    dA, dB = _dev(A), _dev(B)
+    outs = []
+    for variant in ("mfma", tile, "mfma_staged", "mfma_unpadded"):
+        dC = torch.full((w.M, w.N), float("nan"), dtype=torch.float32, device="cuda")
+        sg.sgemm_run_variant(variant, w.M, w.N, w.K, dA, w.K, dB, w.N, dC, w.N)
+        torch.cuda.synchronize()
+        outs.append(dC.cpu().numpy().tobytes())
+    assert all(o == outs[0] for o in outs[1:])
+
+
+@pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged", "reg", "dbuf"])
 def test_padded_leading_dimensions(variant):
     """NaN in the padding of A and B must not reach C; C's padding is untouched."""
     M, N, K = 200, 136, 72
     g = np.random.default_rng(31)
+    # ld % 4 == 0: the buffer-to-LDS path reads around NaN padding
     A = inputs.padded(inputs.uniform(g, (M, K)), K + 12)
     B = inputs.padded(inputs.uniform(g, (K, N)), N + 8)
     C = _run(A, B, M, N, K, variant=variant, ldc=N + 20)
