@@ -124,6 +124,50 @@ def cpu_baseline(w, target_s: float = 12.0):
                       f"accumulation, {dt:.1f} s on {threads} threads"}
 
 
+def oracle_seconds(w, threads: int, rows: int | None = None) -> tuple[float, int]:
+    """Wall time of the oracle's C pass (no abs-sum) on the first `rows` rows."""
+    import numpy as np
+
+    import oracle
+    from dense_fp32_matrix_03_amd import inputs
+
+    A, B = inputs.make_inputs(w)
+    rows = w.M if rows is None else rows
+    A = np.ascontiguousarray(A[:rows])
+    t = time.perf_counter()
+    oracle.sgemm_f64(A, B, K=w.K, N=w.N, want_sabs=False, threads=threads)
+    return time.perf_counter() - t, rows
+
+
+def workload_table(variant) -> list[dict]:
+    """GPU time of sgemm_run and oracle times, for every workload."""
+    import oracle
+    from dense_fp32_matrix_03_amd import inputs
+
+    cores = oracle.max_threads()
+    rows = []
+    rate1 = None
+    for w in inputs.WORKLOADS:
+        reps = max(5, min(200, int(2e11 / w.flops) + 5))
+        ms, finite = time_gpu(w, variant, reps, 3, warm_seconds=0.3)
+        tf = w.flops / (ms * 1e-3) / 1e12
+        r = {"workload": w.name, "gpu_ms": round(ms, 5), "gpu_tflops": round(tf, 2),
+             "pct_of_peak": round(100 * tf / PEAK_TFLOPS, 1), "output_finite": finite,
+             "cores": cores}
+        if w.check == "full":
+            t1, _ = oracle_seconds(w, 1)
+            tn, _ = oracle_seconds(w, cores)
+            rate1 = w.flops / t1
+            r.update(oracle_1core_s=round(t1, 3), oracle_allcore_s=round(tn, 3))
+        else:
+            tn, _ = oracle_seconds(w, cores)
+            r.update(oracle_allcore_s=round(tn, 3),
+                     oracle_1core_s_extrapolated=round(w.flops / rate1, 1) if rate1 else None)
+        print(json.dumps(r), flush=True)
+        rows.append(r)
+    return rows
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description="single-precision GEMM throughput on MI355X")
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +177,10 @@ def main(argv=None) -> int:
     ap.add_argument("--variant", default="mfma", help="kernel variant (default: sgemm_run's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--table", action="store_true",
+                    help="time every workload on the GPU and the oracle on the host (1 thread "
+                         "and all threads; 8192^3 single-thread extrapolated from the "
+                         "2048^3 rate) and print one JSON line per workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -165,6 +213,10 @@ def main(argv=None) -> int:
     sg.sgemm_create()
     w = inputs.BY_NAME[a.workload]
     variant = sg.VARIANTS[a.variant] if a.variant in sg.VARIANTS else int(a.variant)
+    if a.table:
+        workload_table(variant)
+        sg.sgemm_destroy()
+        return 0
 
     ms, finite = time_gpu(w, variant, a.steps, a.warmup)
     tflops = w.flops / (ms * 1e-3) / 1e12

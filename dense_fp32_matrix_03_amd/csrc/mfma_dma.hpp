@@ -71,7 +71,7 @@ inline bool dma_offsets_fit(long BM, long BK, long lda, long ldb, long BN) {
   return BM * lda * 4 + 4096 < kBufferRecords && BK * ldb * 4 + BN * 4 + 4096 < kBufferRecords;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool SWZ>
+template <int BM, int BN, int BK, int WM, int WN, bool SWZ, bool KFULL, int SCHED>
 __global__ void __launch_bounds__(WM *WN *kWave)
 mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   constexpr int NW = WM * WN;
@@ -128,23 +128,30 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     offB[q] = n0 + c < p.N ? (unsigned)(row * p.ldb + c) * 4u : kOutOfRange;
   }
 
-  // Issue the loads of slice t into LDS stage S.
+  // Issue the loads of slice t into LDS stage S.  A slice at or past the end
+  // of K gets descriptors with no records: every lane reads out of range, so
+  // nothing is fetched and zeros land in a stage nobody reads again.  This
+  // keeps the slice body free of branches, so the scheduler can interleave
+  // these loads with matrix-core instructions.
+  const int nk = (p.K + BK - 1) / BK;
   auto dma = [&](auto S, int t) {
     float *as = S.value ? As1 : As0;
     float *bs = S.value ? Bs1 : Bs0;
     const int k0 = t * BK;
-    const bool tail = k0 + BK > p.K;  // only the last slice can be partial
+    const int records = t < nk ? kBufferRecords : 0;
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(p.A + (long)m0 * p.lda + k0), 0, kBufferRecords, kRawBufferWord3);
+        const_cast<float *>(p.A + (long)m0 * p.lda + (t < nk ? k0 : 0)), 0, records,
+        kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(p.B + (long)k0 * p.ldb + n0), 0, kBufferRecords, kRawBufferWord3);
+        const_cast<float *>(p.B + (long)(t < nk ? k0 : 0) * p.ldb + n0), 0, records,
+        kRawBufferWord3);
 #pragma unroll
     for (int q = 0; q < DAW; ++q) {
       unsigned off = offA[q];
-      if (tail) {
+      if constexpr (!KFULL) {
         int row, kc;
         a_chunk(q, row, kc);
-        if (k0 + kc * 4 >= p.K) off = kOutOfRange;
+        off = k0 + kc * 4 < p.K ? off : kOutOfRange;
       }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ra, (lds_void_t *)(as + (wave + q * NW) * 256), 16, off, 0, 0, 0);
@@ -152,10 +159,10 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
     for (int q = 0; q < DBW; ++q) {
       unsigned off = offB[q];
-      if (tail) {
+      if constexpr (!KFULL) {
         int row, c;
         b_chunk(q, row, c);
-        if (k0 + row >= p.K) off = kOutOfRange;
+        off = k0 + row < p.K ? off : kOutOfRange;
       }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rb, (lds_void_t *)(bs + (wave + q * NW) * 256), 16, off, 0, 0, 0);
@@ -205,11 +212,32 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  const int nk = (p.K + BK - 1) / BK;
   Ops cur, nxt;
 
-  // Slice t lives in stage S; slice t+1 (if any) is already on its way to
-  // stage S^1.
+  // Instruction interleaving inside one group (SCHED = 1): after every two
+  // matrix-core instructions, one of the group's LDS reads (and, in the last
+  // group, first one buffer-to-LDS load per instruction), so that neither
+  // burst leaves the matrix pipe idle.
+  constexpr int NMFMA = 4 * FM * FN;
+  constexpr int NDS = FM + 2 * FN;  // 128-bit A reads + paired 32-bit B reads
+  auto interleave = [&](auto with_dma) {
+    if constexpr (SCHED == 1) {
+      constexpr int nv = decltype(with_dma)::value ? DAW + DBW : 0;
+#pragma unroll
+      for (int q = 0; q < nv; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // matrix core
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+      }
+#pragma unroll
+      for (int q = 0; q < NDS; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
+      constexpr int left = NMFMA - nv - 2 * NDS;
+      if constexpr (left > 0) __builtin_amdgcn_sched_group_barrier(0x008, left, 0);
+    }
+  };
+
   auto slice = [&](auto S, int t) {
     constexpr int s = decltype(S)::value;
     using SN = std::integral_constant<int, s ^ 1>;
@@ -217,25 +245,31 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     for (int g = 0; g < G; ++g) {
       if (g + 1 < G) {
         read_ops(S, g + 1, nxt);
+        mma(cur);
+        interleave(std::false_type());
       } else {
         // All reads of stage S are done and slice t+1 has landed in S^1.
         dma_barrier();
-        if (t + 2 < nk) dma(S, t + 2);
-        if (t + 1 < nk) read_ops(SN(), 0, nxt);
+        dma(S, t + 2);
+        read_ops(SN(), 0, nxt);  // harmless if there is no slice t+1
+        mma(cur);
+        interleave(std::true_type());
       }
-      mma(cur);
       cur = nxt;
     }
   };
 
   dma(S0(), 0);
-  if (nk > 1) dma(S1(), 1);
+  dma(S1(), 1);
   dma_barrier();
   read_ops(S0(), 0, cur);
   for (int t = 0; t < nk; t += 2) {
     slice(S0(), t);
     if (t + 1 < nk) slice(S1(), t + 1);
   }
+  // The last slices issued loads past K (zero-filling, no memory traffic);
+  // let them retire before the work-group gives up its LDS.
+  __builtin_amdgcn_s_waitcnt(0x0f70);
 
   const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN + r32;
   const bool full = (m0 + BM <= p.M) && (n0 + BN <= p.N);
@@ -251,12 +285,17 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
       }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool SWZ = true>
+template <int BM, int BN, int BK, int WM, int WN, bool SWZ = true, int SCHED = 1>
 inline hipError_t launch_dma_cfg(const GemmArgs &p, hipStream_t stream, int group_m = 8) {
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const long nwg = (long)tiles_m * tiles_n;
-  hipLaunchKernelGGL((mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ>), dim3((unsigned)nwg),
-                     dim3(WM * WN * kWave), 0, stream, p, tiles_m, tiles_n, group_m);
+  const dim3 grid((unsigned)nwg), block(WM * WN * kWave);
+  if (p.K % BK == 0)
+    hipLaunchKernelGGL((mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, true, SCHED>), grid, block,
+                       0, stream, p, tiles_m, tiles_n, group_m);
+  else
+    hipLaunchKernelGGL((mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, false, SCHED>), grid,
+                       block, 0, stream, p, tiles_m, tiles_n, group_m);
   return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@ namespace sgemm {
 // Tile configurations (block tile, K slice, wave grid), from a sweep over
 // square problems of 1024 .. 8192 on MI355X:
 //   T256  256 x 256 x 32, 2 x 4 waves of 128 x 64  (two waves per SIMD)
-//   T128  128 x 128 x 32, 2 x 4 waves of  64 x 32
+//   T128  128 x 128 x 32, 2 x 2 waves of  64 x 64
 //   T64    64 x  64 x 32, 2 x 2 waves of  32 x 32
 template <int BM, int BN, int BK, int WM, int WN>
 static hipError_t launch_tile(MfmaPath path, const GemmArgs &p, bool va, bool vb,
@@ -19,10 +19,10 @@ static hipError_t launch_tile(MfmaPath path, const GemmArgs &p, bool va, bool vb
   const bool dma = va && vb && dma_offsets_fit(BM, BK, p.lda, p.ldb, BN);
   switch (path) {
     case MfmaPath::Auto:
-      if (dma) return launch_dma_cfg<BM, BN, BK, WM, WN, true>(p, stream);
+      if (dma) return launch_dma_cfg<BM, BN, BK, WM, WN, true, 1>(p, stream);
       return launch_staged_cfg<BM, BN, BK, WM, WN, 4, kStoreGroup>(p, va, vb, stream);
     case MfmaPath::Unpadded:
-      if (dma) return launch_dma_cfg<BM, BN, BK, WM, WN, false>(p, stream);
+      if (dma) return launch_dma_cfg<BM, BN, BK, WM, WN, false, 1>(p, stream);
       return launch_staged_cfg<BM, BN, BK, WM, WN, 0, kStoreGroup>(p, va, vb, stream);
     case MfmaPath::Staged:
       return launch_staged_cfg<BM, BN, BK, WM, WN, 4, kStoreGroup>(p, va, vb, stream);
@@ -41,7 +41,7 @@ hipError_t launch_mfma(MfmaTile tile, MfmaPath path, const GemmArgs &p, bool va,
                        hipStream_t stream) {
   switch (tile) {
     case MfmaTile::T256: return launch_tile<256, 256, 32, 2, 4>(path, p, va, vb, stream);
-    case MfmaTile::T128: return launch_tile<128, 128, 32, 2, 4>(path, p, va, vb, stream);
+    case MfmaTile::T128: return launch_tile<128, 128, 32, 2, 2>(path, p, va, vb, stream);
     case MfmaTile::T64: return launch_tile<64, 64, 32, 2, 2>(path, p, va, vb, stream);
   }
   return hipErrorInvalidValue;
