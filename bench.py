@@ -35,14 +35,18 @@ COUNTERS = os.path.join(ROOT, "profiles", "mfma_gemm_8192_hbm_counters.json")
 COPY_BYTES = 256 << 20  # bytes read (and written) by the copy-calibration kernel
 
 
+# Sources that define the kernel sgemm_run launches for aligned operands (its
+# template, its shared helpers and the file that picks its configuration).
+HOT_KERNEL_SOURCES = ("common.hpp", "mfma_dma.hpp", "mfma_kernels.hip")
+
+
 def kernel_source_digest() -> str:
-    """Digest of the HIP sources; HBM counters are valid only for this digest."""
+    """Digest of the hot kernel's sources; HBM counters are valid only for it."""
     csrc = os.path.join(ROOT, "dense_fp32_matrix_03_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in HOT_KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
@@ -168,6 +172,26 @@ def workload_table(variant) -> list[dict]:
     return rows
 
 
+LADDER = ("naive", "lds", "reg", "dbuf", "mfma_unpadded", "mfma_staged", "mfma")
+
+
+def ladder(w, steps: int, warmup: int, settle: float) -> list[dict]:
+    """Time the pages' progression and the matrix-core steps on one workload."""
+    import dense_fp32_matrix_03_amd as sg
+
+    rows = []
+    for name in LADDER:
+        v = sg.VARIANTS[name]
+        ms, finite = time_gpu(w, v, steps, warmup, warm_seconds=settle)
+        tf = w.flops / (ms * 1e-3) / 1e12
+        r = {"workload": w.name, "variant": sg.sgemm_variant_name(v), "ms": round(ms, 5),
+             "tflops": round(tf, 3), "pct_of_peak": round(100 * tf / PEAK_TFLOPS, 2),
+             "output_finite": finite}
+        print(json.dumps(r), flush=True)
+        rows.append(r)
+    return rows
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description="single-precision GEMM throughput on MI355X")
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +201,11 @@ def main(argv=None) -> int:
     ap.add_argument("--variant", default="mfma", help="kernel variant (default: sgemm_run's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--ladder", action="store_true",
+                    help="time every rung of the vector-FMA ladder and the matrix-core "
+                         "variants on --workload (default here: 2048^3), one JSON line each")
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed calls before each --ladder timing")
     ap.add_argument("--table", action="store_true",
                     help="time every workload on the GPU and the oracle on the host (1 thread "
                          "and all threads; 8192^3 single-thread extrapolated from the "
@@ -215,6 +244,11 @@ def main(argv=None) -> int:
     variant = sg.VARIANTS[a.variant] if a.variant in sg.VARIANTS else int(a.variant)
     if a.table:
         workload_table(variant)
+        sg.sgemm_destroy()
+        return 0
+    if a.ladder:
+        wl = w if a.workload != HEADLINE else inputs.BY_NAME[SECONDARY]
+        ladder(wl, a.steps, a.warmup, a.settle)
         sg.sgemm_destroy()
         return 0
 

@@ -21,10 +21,13 @@
 // of 16) consecutive rows hit disjoint banks.  B stays row-major.
 //
 // Edges.  The buffer descriptor's range check turns a load at an offset
-// past num_records into zeros; a chunk outside the M x K (or K x N) matrix is
-// given such an offset, so ragged tiles and the K tail are zero-filled by the
-// hardware.  Chunks are 4 floats, so this path needs K % 4 == 0 and N % 4 ==
-// 0 and 16-byte aligned operands; other shapes use the register-staged kernel.
+// past num_records into zeros; an element outside the M x K (or K x N)
+// matrix is given such an offset, so ragged tiles and the K tail are
+// zero-filled by the hardware.  An operand that is 16-byte aligned with a
+// leading dimension and width that are multiples of 4 is fetched in 16-byte
+// chunks (64 lanes x 16 B = one 1 KiB block per instruction); any other
+// operand in single floats (256 B per instruction), which handles any
+// alignment and any K.
 #pragma once
 
 #include <type_traits>
@@ -65,25 +68,39 @@ __device__ __forceinline__ void dma_barrier() {
   __syncthreads();
 }
 
+// One wave-wide buffer-to-LDS load: lane l's 16 (WIDE) or 4 bytes at byte
+// offset `off` of the buffer land at LDS address lds + 16 l (or 4 l).
+template <bool WIDE>
+__device__ __forceinline__ void lds_dma(__amdgpu_buffer_rsrc_t r, float *lds, unsigned off) {
+  if constexpr (WIDE)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, off, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 4, off, 0, 0, 0);
+}
+
 // Host-side limit of the path: every in-range offset of a slice must stay
 // below kBufferRecords.
 inline bool dma_offsets_fit(long BM, long BK, long lda, long ldb, long BN) {
   return BM * lda * 4 + 4096 < kBufferRecords && BK * ldb * 4 + BN * 4 + 4096 < kBufferRecords;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool SWZ, bool KFULL, int SCHED>
+// VA / VB: A / B are fetched in 16-byte chunks (16-byte aligned, ld % 4 == 0
+// and K % 4 == 0 for A, N % 4 == 0 for B), else in single floats.
+template <int BM, int BN, int BK, int WM, int WN, bool SWZ, bool KFULL, int SCHED, bool VA,
+          bool VB>
 __global__ void __launch_bounds__(WM *WN *kWave)
 mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int KH = BK / 2, G = KH / 4;
-  constexpr int CPR_A = BK / 4, RPD_A = kWave / CPR_A;  // chunks per row, rows per block
-  constexpr int CPR_B = BN / 4, RPD_B = kWave / CPR_B;
-  constexpr int DA = BM * BK / 256, DB = BK * BN / 256;  // 1 KiB blocks per slice
+  // Each lane of a load moves EA (EB) floats; a block of one wave-wide load
+  // covers 64*EA (64*EB) consecutive floats of the LDS image.
+  constexpr int EA = VA ? 4 : 1, EB = VB ? 4 : 1;
+  constexpr int FPB_A = kWave * EA, FPB_B = kWave * EB;
+  constexpr int DA = BM * BK / FPB_A, DB = BK * BN / FPB_B;  // blocks per slice
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(G >= 2, "BK must be 16 or 32");
-  static_assert(kWave % CPR_B == 0, "a B row must fit a 1 KiB block");
   static_assert(DA % NW == 0 && DB % NW == 0, "blocks must split evenly over the waves");
   constexpr int DAW = DA / NW, DBW = DB / NW;
 
@@ -102,29 +119,38 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // Per-lane byte offsets of the chunks this wave fetches, relative to the
-  // slice origin (row m0 / column k0 of A; row k0 / column n0 of B).  Chunks
-  // in rows of A past M or columns of B past N get the out-of-range offset
-  // once and for all; the K tail is handled per slice.
-  auto a_chunk = [&](int q, int &row, int &kc) {
-    row = (wave + q * NW) * RPD_A + lane / CPR_A;
-    kc = (lane % CPR_A) ^ a_swizzle<BK, SWZ>(row);
+  // Slice element fetched by this lane in the wave's q-th block: row and
+  // column within the slice (A: row of the m tile, k; B: k, column of the n
+  // tile).  The LDS image is A row-major with its 16-byte chunks swizzled,
+  // B row-major; a lane's LDS position is fixed, so it fetches whichever
+  // element belongs there.
+  auto a_elem = [&](int q, int &row, int &k) {
+    const int f = (wave + q * NW) * FPB_A + lane * EA;  // LDS position in the slice
+    row = f / BK;
+    const int pc = f % BK;
+    k = 4 * ((pc / 4) ^ a_swizzle<BK, SWZ>(row)) + pc % 4;
   };
-  auto b_chunk = [&](int q, int &row, int &c) {
-    row = (wave + q * NW) * RPD_B + lane / CPR_B;
-    c = (lane % CPR_B) * 4;
+  auto b_elem = [&](int q, int &row, int &c) {
+    const int f = (wave + q * NW) * FPB_B + lane * EB;
+    row = f / BN;
+    c = f % BN;
   };
+
+  // Per-lane byte offsets relative to the slice origin (row m0 / column k0
+  // of A; row k0 / column n0 of B).  Elements in rows of A past M or columns
+  // of B past N get the out-of-range offset once and for all; the K tail is
+  // handled per slice.
   unsigned offA[DAW], offB[DBW];
 #pragma unroll
   for (int q = 0; q < DAW; ++q) {
-    int row, kc;
-    a_chunk(q, row, kc);
-    offA[q] = m0 + row < p.M ? (unsigned)(row * p.lda + kc * 4) * 4u : kOutOfRange;
+    int row, k;
+    a_elem(q, row, k);
+    offA[q] = m0 + row < p.M ? (unsigned)(row * p.lda + k) * 4u : kOutOfRange;
   }
 #pragma unroll
   for (int q = 0; q < DBW; ++q) {
     int row, c;
-    b_chunk(q, row, c);
+    b_elem(q, row, c);
     offB[q] = n0 + c < p.N ? (unsigned)(row * p.ldb + c) * 4u : kOutOfRange;
   }
 
@@ -149,23 +175,21 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     for (int q = 0; q < DAW; ++q) {
       unsigned off = offA[q];
       if constexpr (!KFULL) {
-        int row, kc;
-        a_chunk(q, row, kc);
-        off = k0 + kc * 4 < p.K ? off : kOutOfRange;
+        int row, k;
+        a_elem(q, row, k);
+        off = k0 + k < p.K ? off : kOutOfRange;
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_void_t *)(as + (wave + q * NW) * 256), 16, off, 0, 0, 0);
+      lds_dma<VA>(ra, as + (wave + q * NW) * FPB_A, off);
     }
 #pragma unroll
     for (int q = 0; q < DBW; ++q) {
       unsigned off = offB[q];
       if constexpr (!KFULL) {
         int row, c;
-        b_chunk(q, row, c);
+        b_elem(q, row, c);
         off = k0 + row < p.K ? off : kOutOfRange;
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (lds_void_t *)(bs + (wave + q * NW) * 256), 16, off, 0, 0, 0);
+      lds_dma<VB>(rb, bs + (wave + q * NW) * FPB_B, off);
     }
   };
 
@@ -222,7 +246,8 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   constexpr int NDS = FM + 2 * FN;  // 128-bit A reads + paired 32-bit B reads
   auto interleave = [&](auto with_dma) {
     if constexpr (SCHED == 1) {
-      constexpr int nv = decltype(with_dma)::value ? DAW + DBW : 0;
+      constexpr int nvm = decltype(with_dma)::value ? DAW + DBW : 0;
+      constexpr int nv = nvm < NMFMA - 2 * NDS ? nvm : NMFMA - 2 * NDS;
 #pragma unroll
       for (int q = 0; q < nv; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // matrix core
@@ -285,17 +310,37 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
       }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool SWZ = true, int SCHED = 1>
-inline hipError_t launch_dma_cfg(const GemmArgs &p, hipStream_t stream, int group_m = 8) {
+template <int BM, int BN, int BK, int WM, int WN, bool SWZ, int SCHED, bool VA, bool VB>
+inline void launch_dma_kernel(const GemmArgs &p, hipStream_t stream, int group_m) {
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-  const long nwg = (long)tiles_m * tiles_n;
-  const dim3 grid((unsigned)nwg), block(WM * WN * kWave);
+  const dim3 grid((unsigned)((long)tiles_m * tiles_n)), block(WM * WN * kWave);
   if (p.K % BK == 0)
-    hipLaunchKernelGGL((mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, true, SCHED>), grid, block,
-                       0, stream, p, tiles_m, tiles_n, group_m);
-  else
-    hipLaunchKernelGGL((mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, false, SCHED>), grid,
+    hipLaunchKernelGGL((mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, true, SCHED, VA, VB>), grid,
                        block, 0, stream, p, tiles_m, tiles_n, group_m);
+  else
+    hipLaunchKernelGGL((mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, false, SCHED, VA, VB>),
+                       grid, block, 0, stream, p, tiles_m, tiles_n, group_m);
+}
+
+// WIDE_ONLY instantiates only the 16-byte-load form; the caller guarantees
+// va && vb.
+template <int BM, int BN, int BK, int WM, int WN, bool SWZ = true, int SCHED = 1,
+          bool WIDE_ONLY = false>
+inline hipError_t launch_dma_cfg(const GemmArgs &p, bool va, bool vb, hipStream_t stream,
+                                 int group_m = 8) {
+  if constexpr (WIDE_ONLY) {
+    if (!(va && vb)) return hipErrorInvalidValue;
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true>(p, stream, group_m);
+  } else {
+    if (va && vb)
+      launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true>(p, stream, group_m);
+    else if (va)
+      launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, false>(p, stream, group_m);
+    else if (vb)
+      launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, true>(p, stream, group_m);
+    else
+      launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, false>(p, stream, group_m);
+  }
   return hipGetLastError();
 }
 

@@ -12,17 +12,19 @@ namespace sgemm {
 //   T256  256 x 256 x 32, 2 x 4 waves of 128 x 64  (two waves per SIMD)
 //   T128  128 x 128 x 32, 2 x 2 waves of  64 x 64
 //   T64    64 x  64 x 32, 2 x 2 waves of  32 x 32
-template <int BM, int BN, int BK, int WM, int WN>
+// WIDE_ONLY: only the 16-byte-load forms are instantiated (the caller
+// guarantees va && vb).
+template <int BM, int BN, int BK, int WM, int WN, bool WIDE_ONLY = false>
 static hipError_t launch_tile(MfmaPath path, const GemmArgs &p, bool va, bool vb,
                               hipStream_t stream) {
   constexpr int kStoreGroup = 1;  // staged kernel: write the next slice after group 1 of 4
-  const bool dma = va && vb && dma_offsets_fit(BM, BK, p.lda, p.ldb, BN);
+  const bool dma = dma_offsets_fit(BM, BK, p.lda, p.ldb, BN);
   switch (path) {
     case MfmaPath::Auto:
-      if (dma) return launch_dma_cfg<BM, BN, BK, WM, WN, true, 1>(p, stream);
+      if (dma) return launch_dma_cfg<BM, BN, BK, WM, WN, true, 1, WIDE_ONLY>(p, va, vb, stream);
       return launch_staged_cfg<BM, BN, BK, WM, WN, 4, kStoreGroup>(p, va, vb, stream);
     case MfmaPath::Unpadded:
-      if (dma) return launch_dma_cfg<BM, BN, BK, WM, WN, false, 1>(p, stream);
+      if (dma) return launch_dma_cfg<BM, BN, BK, WM, WN, false, 1, WIDE_ONLY>(p, va, vb, stream);
       return launch_staged_cfg<BM, BN, BK, WM, WN, 0, kStoreGroup>(p, va, vb, stream);
     case MfmaPath::Staged:
       return launch_staged_cfg<BM, BN, BK, WM, WN, 4, kStoreGroup>(p, va, vb, stream);
@@ -40,7 +42,11 @@ MfmaTile choose_mfma_tile(long M, long N, int cus) {
 hipError_t launch_mfma(MfmaTile tile, MfmaPath path, const GemmArgs &p, bool va, bool vb,
                        hipStream_t stream) {
   switch (tile) {
-    case MfmaTile::T256: return launch_tile<256, 256, 32, 2, 4>(path, p, va, vb, stream);
+    case MfmaTile::T256:
+      // The 256 x 256 tile keeps 128 accumulators per lane; its 4-byte-load
+      // forms would spill, so operands that need them take the 128 x 128 tile.
+      if (!(va && vb)) return launch_tile<128, 128, 32, 2, 2>(path, p, va, vb, stream);
+      return launch_tile<256, 256, 32, 2, 4, true>(path, p, va, vb, stream);
     case MfmaTile::T128: return launch_tile<128, 128, 32, 2, 2>(path, p, va, vb, stream);
     case MfmaTile::T64: return launch_tile<64, 64, 32, 2, 2>(path, p, va, vb, stream);
   }
