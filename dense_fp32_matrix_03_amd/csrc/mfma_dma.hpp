@@ -246,8 +246,7 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   constexpr int NDS = FM + 2 * FN;  // 128-bit A reads + paired 32-bit B reads
   auto interleave = [&](auto with_dma) {
     if constexpr (SCHED == 1) {
-      constexpr int nvm = decltype(with_dma)::value ? DAW + DBW : 0;
-      constexpr int nv = nvm < NMFMA - 2 * NDS ? nvm : NMFMA - 2 * NDS;
+      constexpr int nv = decltype(with_dma)::value ? DAW + DBW : 0;
 #pragma unroll
       for (int q = 0; q < nv; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // matrix core
