@@ -11,6 +11,9 @@ What is here:
   double products A(i,k) * B(k,j), plus the sum of their absolute values.
   The definition is the summation formula of the article "硬件加速原理：CUDA核函数
   优化矩阵乘法的内存访问模式", section "矩阵乘法的计算特性".
+* ``sgemm_ex_f64`` -- the general form C = alpha op(A) op(B) + beta C0 with
+  optionally transposed operands; the same exact-product, ascending-k double
+  sum, then alpha * sum + beta * C0, with scale |alpha| S + |beta| |C0|.
 * ``check`` -- the per-element acceptance test
   |C - Cref| <= 1e-5 * sum_k |A(i,k) B(k,j)| + 1e-6, with C finite.
 * ``freivalds`` -- a whole-matrix necessary condition of that test, used at
@@ -67,6 +70,10 @@ def _load():
     lib.oracle_sgemm_f64.restype = ctypes.c_int
     lib.oracle_entries_f64.argtypes = [i64, i64, i64, fp, i64, fp, i64, i64, fp, fp, dp, dp]
     lib.oracle_entries_f64.restype = ctypes.c_int
+    lib.oracle_sgemm_ex_f64.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                                        ctypes.c_double, fp, i64, fp, i64, ctypes.c_double,
+                                        fp, i64, dp, i64, dp, i64, ctypes.c_int]
+    lib.oracle_sgemm_ex_f64.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -111,6 +118,32 @@ def sgemm_f64(A: np.ndarray, B: np.ndarray, K: int | None = None, N: int | None 
                                   _ptr(S) if S is not None else None, max(1, N), int(threads))
     if rc != 0:
         raise ValueError(f"oracle_sgemm_f64 rejected its arguments (rc={rc})")
+    return C, S
+
+
+def sgemm_ex_f64(transA: bool, transB: bool, M: int, N: int, K: int, alpha: float,
+                 A: np.ndarray, B: np.ndarray, beta: float = 0.0, C0: np.ndarray | None = None,
+                 threads: int = 0):
+    """Return (Cref, Sabs) for C = alpha op(A) op(B) + beta C0 (float64, M x N).
+
+    A is stored as an array of shape (K, lda) when transA else (M, lda); B as
+    (N, ldb) when transB else (K, ldb).  C0 is float32 of shape (M, ldc0);
+    it is not read when beta == 0.
+    """
+    A, lda = _as_f32(A, K if transA else M, M if transA else K, "A")
+    B, ldb = _as_f32(B, N if transB else K, K if transB else N, "B")
+    if beta != 0.0:
+        C0, ldc0 = _as_f32(C0, M, N, "C0")
+    else:
+        C0, ldc0 = None, max(1, N)
+    C = np.empty((M, N), dtype=np.float64)
+    S = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_sgemm_ex_f64(int(transA), int(transB), M, N, K, float(alpha), _ptr(A),
+                                     lda, _ptr(B), ldb, float(beta),
+                                     _ptr(C0) if C0 is not None else None, ldc0, _ptr(C),
+                                     max(1, N), _ptr(S), max(1, N), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_sgemm_ex_f64 rejected its arguments (rc={rc})")
     return C, S
 
 

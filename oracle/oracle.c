@@ -124,6 +124,58 @@ int oracle_entries_f64(int64_t M, int64_t N, int64_t K,
     return ORACLE_OK;
 }
 
+/*
+ * The general form C = alpha * op(A) op(B) + beta * C0.  op(A)(i,k) is
+ * A[i*lda + k], or A[k*lda + i] when transA; op(B)(k,j) is B[k*ldb + j], or
+ * B[j*ldb + k] when transB.  The sum over k is formed exactly as in
+ * oracle_sgemm_f64 (exact double products, ascending k, double sums); then
+ * Cref = alpha * sum + beta * C0, in double.  When beta == 0, C0 is not read
+ * (it may be NULL or hold NaN).  Sabs (may be NULL) receives
+ * |alpha| * sum_k |op(A)(i,k) op(B)(k,j)| + |beta| * |C0(i,j)|, the scale of
+ * the tolerance for this form.  The definition is the plain product's (see
+ * the top of this file) with the transposed indexing spelled out above.
+ */
+int oracle_sgemm_ex_f64(int transA, int transB, int64_t M, int64_t N, int64_t K, double alpha,
+                        const float *A, int64_t lda, const float *B, int64_t ldb, double beta,
+                        const float *C0, int64_t ldc0, double *Cref, int64_t ldr,
+                        double *Sabs, int64_t lds, int nthreads)
+{
+    const int64_t acols = transA ? M : K, bcols = transB ? K : N;
+    if (M < 0 || N < 0 || K < 0) return ORACLE_BAD_ARG;
+    if (lda < (acols > 1 ? acols : 1) || ldb < (bcols > 1 ? bcols : 1)) return ORACLE_BAD_ARG;
+    if (ldr < (N > 1 ? N : 1) || (Sabs && lds < (N > 1 ? N : 1))) return ORACLE_BAD_ARG;
+    if (beta != 0.0 && ldc0 < (N > 1 ? N : 1)) return ORACLE_BAD_ARG;
+    if (M == 0 || N == 0) return ORACLE_OK;
+    if (!Cref || (K > 0 && (!A || !B)) || (beta != 0.0 && !C0)) return ORACLE_BAD_ARG;
+
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < M; ++i) {
+        double *c = Cref + i * ldr;
+        double *s = Sabs ? Sabs + i * lds : NULL;
+        for (int64_t j = 0; j < N; ++j) c[j] = 0.0;
+        if (s)
+            for (int64_t j = 0; j < N; ++j) s[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = (double)(transA ? A[k * lda + i] : A[i * lda + k]);
+            for (int64_t j = 0; j < N; ++j) {
+                const double b = (double)(transB ? B[j * ldb + k] : B[k * ldb + j]);
+                const double prod = a * b;
+                c[j] += prod;
+                if (s) s[j] += fabs(prod);
+            }
+        }
+        for (int64_t j = 0; j < N; ++j) {
+            const double c0 = beta != 0.0 ? (double)C0[i * ldc0 + j] : 0.0;
+            c[j] = alpha * c[j] + beta * c0;
+            if (s) s[j] = fabs(alpha) * s[j] + fabs(beta) * fabs(c0);
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* Threads OpenMP would use by default; 1 when built without OpenMP. */
 int oracle_max_threads(void)
 {

@@ -276,3 +276,86 @@ def test_inputs_deterministic_and_in_range():
     A4, B4 = inputs.make_inputs(w4)
     assert A4.shape == (1000, 777) and B4.shape == (777, 1500)
     assert abs(float(A4.mean())) < 0.01 and abs(float(A4.std()) - 1) < 0.01
+
+
+# -- the general form: C = alpha op(A) op(B) + beta C0 -------------------------------
+
+def test_general_plain_case_equals_plain_product():
+    g = np.random.default_rng(61)
+    A = inputs.uniform(g, (33, 47))
+    B = inputs.normal(g, (47, 29))
+    C1, S1 = oracle.sgemm_ex_f64(False, False, 33, 29, 47, 1.0, A, B)
+    C0, S0 = oracle.sgemm_f64(A, B)
+    assert np.array_equal(C1, C0) and np.array_equal(S1, S0)
+
+
+@pytest.mark.parametrize("ta,tb", [(False, True), (True, False), (True, True)])
+def test_general_transposed_storage_equals_plain(ta, tb):
+    """Passing the stored transpose with the flag set gives the same bits."""
+    g = np.random.default_rng(67)
+    M, N, K = 21, 34, 13
+    A = inputs.uniform(g, (M, K))
+    B = inputs.uniform(g, (K, N))
+    As = np.ascontiguousarray(A.T) if ta else A
+    Bs = np.ascontiguousarray(B.T) if tb else B
+    C1, S1 = oracle.sgemm_ex_f64(ta, tb, M, N, K, 1.0, As, Bs)
+    C0, S0 = oracle.sgemm_f64(A, B)
+    assert np.array_equal(C1, C0) and np.array_equal(S1, S0)
+
+
+def test_general_brute_force_with_transposes_and_scalars():
+    """Exact rationals on small shapes, every layout, dyadic alpha and beta."""
+    from fractions import Fraction
+    g = np.random.default_rng(71)
+    for ta in (False, True):
+        for tb in (False, True):
+            for (M, N, K) in [(1, 1, 1), (3, 2, 5), (4, 6, 3), (5, 5, 7)]:
+                alpha, beta = -1.25, 0.5
+                A = inputs.uniform(g, (K, M) if ta else (M, K))
+                B = inputs.uniform(g, (N, K) if tb else (K, N))
+                C0 = inputs.uniform(g, (M, N))
+                Cref, Sabs = oracle.sgemm_ex_f64(ta, tb, M, N, K, alpha, A, B, beta, C0)
+                opA = A.T if ta else A
+                opB = B.T if tb else B
+                exact = oracle.exact_products(np.ascontiguousarray(opA), np.ascontiguousarray(opB))
+                for i in range(M):
+                    for j in range(N):
+                        e = Fraction(alpha) * exact[i][j] + Fraction(beta) * Fraction(float(C0[i, j]))
+                        err = abs(float(e - Fraction(Cref[i, j])))
+                        assert err <= (K + 4) * 2.0 ** -53 * Sabs[i, j], (ta, tb, M, N, K, i, j)
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False), (True, True)])
+def test_general_integer_inputs_exact_vs_int64(ta, tb):
+    g = np.random.default_rng(73)
+    M, N, K = 70, 90, 130
+    A = inputs.small_integers(g, (K, M) if ta else (M, K))
+    B = inputs.small_integers(g, (N, K) if tb else (K, N))
+    C0 = inputs.small_integers(g, (M, N), -100, 100)
+    Cref, Sabs = oracle.sgemm_ex_f64(ta, tb, M, N, K, 3.0, A, B, -2.0, C0)
+    opA = (A.T if ta else A).astype(np.int64)
+    opB = (B.T if tb else B).astype(np.int64)
+    expect = 3 * (opA @ opB) - 2 * C0.astype(np.int64)
+    assert np.array_equal(Cref, expect.astype(np.float64))
+
+
+def test_general_beta_zero_does_not_read_c_and_alpha_zero_scales():
+    g = np.random.default_rng(79)
+    A = inputs.uniform(g, (8, 9))
+    B = inputs.uniform(g, (9, 10))
+    nan = np.full((8, 10), np.nan, dtype=np.float32)
+    C1, _ = oracle.sgemm_ex_f64(False, False, 8, 10, 9, 2.0, A, B, 0.0, nan)
+    assert np.all(np.isfinite(C1))
+    C0 = inputs.uniform(g, (8, 10))
+    C2, S2 = oracle.sgemm_ex_f64(False, False, 8, 10, 9, 0.0, A, B, 0.75, C0)
+    assert np.array_equal(C2, 0.75 * C0.astype(np.float64))
+    assert np.array_equal(S2, 0.75 * np.abs(C0.astype(np.float64)))
+
+
+def test_pins_catch_a_wrong_transpose_flag():
+    g = np.random.default_rng(83)
+    A = inputs.uniform(g, (6, 6))
+    B = inputs.uniform(g, (6, 6))
+    right, _ = oracle.sgemm_ex_f64(False, False, 6, 6, 6, 1.0, A, B)
+    wrong, _ = oracle.sgemm_ex_f64(True, False, 6, 6, 6, 1.0, A, B)
+    assert not np.array_equal(right, wrong)
