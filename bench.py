@@ -192,6 +192,78 @@ def ladder(w, steps: int, warmup: int, settle: float) -> list[dict]:
     return rows
 
 
+# General-form cases: (name, transA, transB, M, N, K, alpha, beta, batch).
+GENERAL = (
+    ("nn_2048", 0, 0, 2048, 2048, 2048, 1.0, 0.0, 1),
+    ("nt_2048", 0, 1, 2048, 2048, 2048, 1.0, 0.0, 1),
+    ("tn_2048", 1, 0, 2048, 2048, 2048, 1.0, 0.0, 1),
+    ("tt_2048", 1, 1, 2048, 2048, 2048, 1.0, 0.0, 1),
+    ("nn_2048_alpha_beta", 0, 0, 2048, 2048, 2048, 1.5, 0.5, 1),
+    ("nn_8192", 0, 0, 8192, 8192, 8192, 1.0, 0.0, 1),
+    ("nt_8192", 0, 1, 8192, 8192, 8192, 1.0, 0.0, 1),
+    ("tn_8192", 1, 0, 8192, 8192, 8192, 1.0, 0.0, 1),
+    ("tt_8192", 1, 1, 8192, 8192, 8192, 1.0, 0.0, 1),
+    ("nn_8192_alpha_beta", 0, 0, 8192, 8192, 8192, 1.5, 0.5, 1),
+    ("batched_64x512", 0, 0, 512, 512, 512, 1.0, 0.0, 64),
+    ("batched_16x1024_nt", 0, 1, 1024, 1024, 1024, 1.0, 0.0, 16),
+    ("batched_1024x64", 0, 0, 64, 64, 64, 1.0, 0.0, 1024),
+)
+
+
+def general_table(settle: float) -> list[dict]:
+    """Time sgemm_run_strided_batched on the GENERAL cases (uniform inputs,
+    packed operands), one JSON line each."""
+    import numpy as np
+    import torch
+
+    import dense_fp32_matrix_03_amd as sg
+    from dense_fp32_matrix_03_amd import inputs
+
+    rows = []
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    for name, ta, tb, M, N, K, alpha, beta, batch in GENERAL:
+        g = np.random.default_rng(7)
+        ar, ac = (K, M) if ta else (M, K)
+        br, bc = (N, K) if tb else (K, N)
+        dA = torch.from_numpy(inputs.uniform(g, (batch, ar, ac))).cuda()
+        dB = torch.from_numpy(inputs.uniform(g, (batch, br, bc))).cuda()
+        dC = torch.from_numpy(inputs.uniform(g, (batch, M, N))).cuda()
+
+        def step():
+            sg.sgemm_run_strided_batched(ta, tb, M, N, K, alpha, dA, ac, ar * ac, dB, bc,
+                                         br * bc, beta, dC, N, M * N, batch, h)
+
+        flops = 2.0 * M * N * K * batch
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        t_end = time.perf_counter() + settle
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                step()
+            torch.cuda.synchronize()
+        steps = max(10, min(200, int(4e12 / flops)))
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps):
+            step()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        tf = flops / (ms * 1e-3) / 1e12
+        r = {"case": name, "transA": ta, "transB": tb, "M": M, "N": N, "K": K, "alpha": alpha,
+             "beta": beta, "batch": batch, "ms": round(ms, 5), "tflops": round(tf, 2),
+             "pct_of_peak": round(100 * tf / PEAK_TFLOPS, 1),
+             "output_finite": bool(torch.isfinite(dC).all().item())}
+        print(json.dumps(r), flush=True)
+        rows.append(r)
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description="single-precision GEMM throughput on MI355X")
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +282,9 @@ def main(argv=None) -> int:
                     help="time every workload on the GPU and the oracle on the host (1 thread "
                          "and all threads; 8192^3 single-thread extrapolated from the "
                          "2048^3 rate) and print one JSON line per workload")
+    ap.add_argument("--general", action="store_true",
+                    help="time the general form (transposes, alpha/beta, strided batches) "
+                         "on a fixed set of cases, one JSON line each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -244,6 +319,10 @@ def main(argv=None) -> int:
     variant = sg.VARIANTS[a.variant] if a.variant in sg.VARIANTS else int(a.variant)
     if a.table:
         workload_table(variant)
+        sg.sgemm_destroy()
+        return 0
+    if a.general:
+        general_table(a.settle)
         sg.sgemm_destroy()
         return 0
     if a.ladder:

@@ -65,6 +65,12 @@ def load_library(path: str = LIB_PATH):
     lib.sgemm_run.restype = ci
     lib.sgemm_run_variant.argtypes = [ci] + gemm_args
     lib.sgemm_run_variant.restype = ci
+    f32 = ctypes.c_float
+    lib.sgemm_run_ex.argtypes = [ci, ci, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, vp]
+    lib.sgemm_run_ex.restype = ci
+    lib.sgemm_run_strided_batched.argtypes = [ci, ci, i64, i64, i64, f32, vp, i64, i64, vp, i64,
+                                              i64, f32, vp, i64, i64, i64, vp]
+    lib.sgemm_run_strided_batched.restype = ci
     lib.sgemm_mfma_probe.argtypes = [ci, vp, vp, vp, vp]
     lib.sgemm_mfma_probe.restype = ci
     lib.sgemm_status_string.argtypes = [ci]
@@ -120,6 +126,22 @@ def sgemm_run_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> 
     v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     _check("sgemm_run_variant", load_library().sgemm_run_variant(
         v, M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _stream(stream)))
+
+
+def sgemm_run_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                 stream=None) -> None:
+    """C = alpha op(A) op(B) + beta C (op = transpose when the flag is set)."""
+    _check("sgemm_run_ex", load_library().sgemm_run_ex(
+        int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
+        float(beta), _ptr(C), ldc, _stream(stream)))
+
+
+def sgemm_run_strided_batched(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb,
+                              strideB, beta, C, ldc, strideC, batch, stream=None) -> None:
+    """`batch` general products, operands `stride*` floats apart."""
+    _check("sgemm_run_strided_batched", load_library().sgemm_run_strided_batched(
+        int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda, strideA, _ptr(B), ldb,
+        strideB, float(beta), _ptr(C), ldc, strideC, batch, _stream(stream)))
 
 
 def sgemm_mfma_probe(which, A, B, C, stream=None) -> None:

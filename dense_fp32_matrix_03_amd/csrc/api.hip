@@ -112,7 +112,7 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
 
   hipError_t err;
   if (K == 0) {
-    err = sgemm::launch_zero(p, s);
+    err = sgemm::launch_scale(p, s);  // beta = 0: zeros
   } else {
     const bool va = aligned16(A) && lda % 4 == 0 && K % 4 == 0;
     const bool vb = aligned16(B) && ldb % 4 == 0 && N % 4 == 0;
@@ -152,6 +152,74 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
 int sgemm_run(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
               int64_t ldb, float *C, int64_t ldc, void *stream) {
   return sgemm_run_variant(SGEMM_VARIANT_MFMA, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int sgemm_run_strided_batched(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                              float alpha, const float *A, int64_t lda, int64_t strideA,
+                              const float *B, int64_t ldb, int64_t strideB, float beta,
+                              float *C, int64_t ldc, int64_t strideC, int64_t batch,
+                              void *stream) {
+  if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1)) return SGEMM_ERR_INVALID_VALUE;
+  if (M < 0 || N < 0 || K < 0 || batch < 0) return SGEMM_ERR_INVALID_VALUE;
+  if (strideA < 0 || strideB < 0 || strideC < 0) return SGEMM_ERR_INVALID_VALUE;
+  // Distinct products write disjoint C matrices.
+  if (batch > 1 && M > 0 && N > 0 && (__int128)(M - 1) * ldc + N > strideC)
+    return SGEMM_ERR_INVALID_VALUE;
+  const int64_t a_cols = transA ? M : K, b_cols = transB ? K : N;
+  if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1) ||
+      ldc < (N > 1 ? N : 1))
+    return SGEMM_ERR_INVALID_VALUE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim || batch > kMaxDim) return SGEMM_ERR_TOO_LARGE;
+  if (batch > 0 && ((M + 15) / 16) * ((N + 15) / 16) > kMaxDim / batch) return SGEMM_ERR_TOO_LARGE;
+  const bool reads_ab = K > 0 && alpha != 0.f;
+  if (M > 0 && N > 0 && batch > 0) {
+    if (!C) return SGEMM_ERR_INVALID_VALUE;
+    if (reads_ab && (!A || !B)) return SGEMM_ERR_INVALID_VALUE;
+  }
+  if (!g_ready.load(std::memory_order_acquire)) return SGEMM_ERR_NOT_INITIALIZED;
+  if (M == 0 || N == 0 || batch == 0) return SGEMM_OK;
+  DeviceInfo di;
+  int rc = current_device_info(&di);
+  if (rc != SGEMM_OK) return rc;
+
+  sgemm::GemmArgs p;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.A = A;
+  p.lda = lda;
+  p.B = B;
+  p.ldb = ldb;
+  p.C = C;
+  p.ldc = ldc;
+  p.alpha = alpha;
+  p.beta = beta;
+  p.strideA = strideA;
+  p.strideB = strideB;
+  p.strideC = strideC;
+  p.batch = (int)batch;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  hipError_t err;
+  if (!reads_ab) {
+    err = sgemm::launch_scale(p, s);  // C = beta C (zeros when beta == 0)
+  } else {
+    // 16-byte loads need 16-byte aligned bases, strides and leading
+    // dimensions, and a stored width that is a multiple of 4.
+    const bool va = aligned16(A) && lda % 4 == 0 && strideA % 4 == 0 && a_cols % 4 == 0;
+    const bool vb = aligned16(B) && ldb % 4 == 0 && strideB % 4 == 0 && b_cols % 4 == 0;
+    const sgemm::MfmaTile tile = sgemm::choose_mfma_tile(M, N, di.cus, batch);
+    err = sgemm::launch_mfma_general(tile, p, transA, transB, va, vb, s);
+    if (err == hipErrorInvalidValue) return SGEMM_ERR_TOO_LARGE;
+  }
+  return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+int sgemm_run_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                 const float *A, int64_t lda, const float *B, int64_t ldb, float beta, float *C,
+                 int64_t ldc, void *stream) {
+  return sgemm_run_strided_batched(transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C,
+                                   ldc, 0, 1, stream);
 }
 
 int sgemm_mfma_probe(int which, const float *A, const float *B, float *C, void *stream) {

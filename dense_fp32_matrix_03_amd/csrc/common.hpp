@@ -71,6 +71,12 @@ struct GemmArgs {
   long ldb;
   float *C;
   long ldc;
+  // The general form: C = alpha * op(A) op(B) + beta * C over `batch`
+  // products whose operands start strideA / strideB / strideC floats apart.
+  // The plain product keeps these defaults.
+  float alpha = 1.f, beta = 0.f;
+  long strideA = 0, strideB = 0, strideC = 0;
+  int batch = 1;
 };
 
 // Register-staged fetch of a ROWS x COLS window (COLS a multiple of 4) of a

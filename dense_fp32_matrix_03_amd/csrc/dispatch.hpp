@@ -19,13 +19,22 @@ enum class MfmaTile { T256, T128, T64 };
 //            no A row padding), to measure what that layout buys.
 enum class MfmaPath { Auto, Staged, Unpadded };
 
-// Largest tile that still gives at least one work-group per compute unit,
-// else the smallest.
-MfmaTile choose_mfma_tile(long M, long N, int cus);
+// Largest tile that still gives at least one work-group per compute unit
+// over `batch` products, else the smallest.
+MfmaTile choose_mfma_tile(long M, long N, int cus, long batch = 1);
 
 // Matrix-core product.  va / vb: A / B qualify for 128-bit loads.
 hipError_t launch_mfma(MfmaTile tile, MfmaPath path, const GemmArgs &p, bool va, bool vb,
                        hipStream_t stream);
+
+// General product C = alpha op(A) op(B) + beta C over p.batch products on
+// the buffer-to-LDS kernel (ta / tb: A / B stored transposed).  Returns
+// hipErrorInvalidValue if a slice's offsets do not fit a buffer descriptor.
+hipError_t launch_mfma_general(MfmaTile tile, const GemmArgs &p, bool ta, bool tb, bool va,
+                               bool vb, hipStream_t stream);
+
+// C = beta * C over p.batch products (zeros when beta == 0; C not read).
+hipError_t launch_scale(const GemmArgs &p, hipStream_t stream);
 
 // One-instruction lane-layout probe (which: 0 = 32x32x2, 1 = 16x16x4).
 hipError_t launch_mfma_probe(int which, const float *A, const float *B, float *C,
@@ -35,7 +44,5 @@ hipError_t launch_mfma_probe(int which, const float *A, const float *B, float *C
 // 3 register-tiled with a double-buffered LDS pipeline.
 hipError_t launch_valu(int rung, const GemmArgs &p, bool va, bool vb, hipStream_t stream);
 
-// C[0:M, 0:N] = 0 (the K == 0 product).
-hipError_t launch_zero(const GemmArgs &p, hipStream_t stream);
 
 }  // namespace sgemm

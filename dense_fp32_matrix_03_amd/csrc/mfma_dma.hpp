@@ -1,33 +1,44 @@
 // mfma_dma.hpp -- matrix-core product whose K slices reach LDS by direct
-// buffer-to-LDS loads (gfx950 buffer_load_dwordx4 ... lds).
+// buffer-to-LDS loads (gfx950 buffer_load_dword[x4] ... lds).
+//
+// Computes C = alpha * op(A) op(B) + beta * C for one or a strided batch of
+// products; the plain C = A x B is alpha = 1, beta = 0, no transposes, one
+// product.
 //
 // The register-staged kernel spends VGPRs on the next slice, then waits for
 // those loads and writes them to LDS itself; with one wave per SIMD that
 // write-back sits between matrix-core instructions and leaves the matrix
 // pipe idle.  Here each wave only issues the loads: the memory system writes
-// the 16 bytes of lane l to LDS address M0 + 16 l of a 1 KiB block, no VGPR
-// is involved, and the wave carries on with matrix-core work.  The double
-// buffer of the textbook chapter "4. 矩阵乘法性能优化" (section 四) becomes:
-// the loads of slice t+2 go out right after the barrier that ends slice t,
-// into the stage slice t has just released, and the barrier that ends slice
-// t+1 waits for them -- a full slice of latency cover.
+// the bytes of lane l to LDS address M0 + 16 l (or 4 l) of the block, no
+// VGPR is involved, and the wave carries on with matrix-core work.  The
+// double buffer of the textbook chapter "4. 矩阵乘法性能优化" (section 四)
+// becomes: the loads of slice t+2 go out right after the barrier that ends
+// slice t, into the stage slice t has just released, and the barrier that
+// ends slice t+1 waits for them -- a full slice of latency cover.
 //
-// Layout.  A slice of A is BM rows x BK floats, rows packed; a 1 KiB block
-// holds 64/(BK/4) whole rows.  Because a block's LDS image is fixed by lane
-// order, the anti-conflict padding of the chapter (section 三) cannot be
-// used; instead lane l of a block fetches the global chunk whose index is
-// its LDS chunk index XOR a function of the row (a_swizzle).  The swizzle
-// depends only on row mod 16 and makes the 128-bit operand reads of 8 (and
-// of 16) consecutive rows hit disjoint banks.  B stays row-major.
+// Layout.  An operand's slice is BK values of k by D values of m (or n).
+// Where k runs along the stored rows (B as given, or A transposed) the LDS
+// image is the stored window itself, row-major [BK][D], and the operand
+// reads are 32-bit, consecutive lanes on consecutive banks.  Where k runs
+// along the stored columns (A as given, or B transposed) the image is
+// [D][BK] with k contiguous, read 128 bits (four k) at a time; the rows of a
+// 1 KiB load block cannot be padded against bank conflicts as the chapter
+// pads its shared tiles (section 三), because a block's LDS image is fixed by
+// lane order, so instead each lane fetches the global chunk whose index is
+// its LDS chunk index XOR a function of the row (kc_swizzle).  The swizzle
+// depends only on row mod 16 and makes the 128-bit reads of 8 (and of 16)
+// consecutive rows hit disjoint banks.  The article "硬件加速原理：CUDA核函数
+// 优化矩阵乘法的内存访问模式" (section "访问模式对比") makes the same point for
+// row- versus column-major operands: keep the loads contiguous and re-lay
+// the data out on chip.
 //
 // Edges.  The buffer descriptor's range check turns a load at an offset
-// past num_records into zeros; an element outside the M x K (or K x N)
-// matrix is given such an offset, so ragged tiles and the K tail are
+// past num_records into zeros; an element outside op(A) (M x K) or op(B)
+// (K x N) is given such an offset, so ragged tiles and the K tail are
 // zero-filled by the hardware.  An operand that is 16-byte aligned with a
-// leading dimension and width that are multiples of 4 is fetched in 16-byte
-// chunks (64 lanes x 16 B = one 1 KiB block per instruction); any other
-// operand in single floats (256 B per instruction), which handles any
-// alignment and any K.
+// leading dimension and a stored width that are multiples of 4 is fetched in
+// 16-byte chunks (64 lanes x 16 B = one 1 KiB block per instruction); any
+// other operand in single floats (256 B per instruction).
 #pragma once
 
 #include <type_traits>
@@ -38,11 +49,11 @@ namespace sgemm {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Chunk swizzle of row `row` of an A slice with BK floats per row (SWZ =
-// false keeps the plain layout, for measuring what the swizzle buys).
+// Chunk swizzle of row `row` of a k-contiguous slice image with BK floats per
+// row (SWZ = false keeps the plain layout, for measuring what it buys).
 template <int BK, bool SWZ>
-__device__ __forceinline__ int a_swizzle(int row) {
-  static_assert(BK == 16 || BK == 32, "A swizzle is defined for 4 or 8 chunks per row");
+__device__ __forceinline__ int kc_swizzle(int row) {
+  static_assert(BK == 16 || BK == 32, "swizzle is defined for 4 or 8 chunks per row");
   if constexpr (!SWZ)
     return 0;
   else if constexpr (BK == 16)
@@ -53,7 +64,7 @@ __device__ __forceinline__ int a_swizzle(int row) {
 
 // Word 3 of a raw (untyped, unswizzled) buffer descriptor on CDNA.
 constexpr int kRawBufferWord3 = 0x00020000;
-// num_records of the descriptors, and the offset given to chunks that lie
+// num_records of the descriptors, and the offset given to elements that lie
 // outside the matrix: at or past num_records, so they read as zero.
 constexpr int kBufferRecords = 0x7ffff000;
 constexpr unsigned kOutOfRange = 0x80000000u;
@@ -78,31 +89,57 @@ __device__ __forceinline__ void lds_dma(__amdgpu_buffer_rsrc_t r, float *lds, un
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 4, off, 0, 0, 0);
 }
 
-// Host-side limit of the path: every in-range offset of a slice must stay
-// below kBufferRecords.
-inline bool dma_offsets_fit(long BM, long BK, long lda, long ldb, long BN) {
-  return BM * lda * 4 + 4096 < kBufferRecords && BK * ldb * 4 + BN * 4 + 4096 < kBufferRecords;
+// Host-side limit of the path: every in-range offset of a slice (relative to
+// the slice origin) must stay below kBufferRecords.  rows_a / rows_b: stored
+// rows of a slice window (BM, or BK when A is transposed; BK, or BN when B
+// is transposed).
+inline bool dma_offsets_fit(long rows_a, long lda, long rows_b, long ldb) {
+  return rows_a * lda * 4 + 4096 < kBufferRecords && rows_b * ldb * 4 + 4096 < kBufferRecords;
 }
 
-// VA / VB: A / B are fetched in 16-byte chunks (16-byte aligned, ld % 4 == 0
-// and K % 4 == 0 for A, N % 4 == 0 for B), else in single floats.
+// Geometry of one operand's slice: D values of m (or n) by BK values of k.
+// KROWS: k runs along the stored rows.  WIDE: 16-byte loads.
+template <int D, int BK, bool KROWS, bool WIDE, bool SWZ, int NW>
+struct SliceGeom {
+  static constexpr int R = KROWS ? BK : D;  // stored rows of the window
+  static constexpr int W = KROWS ? D : BK;  // stored columns
+  static constexpr int E = WIDE ? 4 : 1;    // floats per lane per load
+  static constexpr int FPB = kWave * E;     // floats per wave-wide load
+  static constexpr int NB = R * W / FPB;    // loads per slice
+  static_assert(NB % NW == 0, "loads must split evenly over the waves");
+  static constexpr int NBW = NB / NW;       // loads per wave per slice
+
+  // Stored (row, col) of the window element that lane `lane` fetches in the
+  // wave's q-th load: whichever element belongs at that lane's LDS position.
+  __device__ __forceinline__ static void elem(int wave, int lane, int q, int &row, int &col) {
+    const int f = (wave + q * NW) * FPB + lane * E;
+    row = f / W;
+    const int pc = f % W;
+    if constexpr (KROWS)
+      col = pc;
+    else
+      col = 4 * ((pc / 4) ^ kc_swizzle<BK, SWZ>(row)) + pc % 4;
+  }
+  __device__ __forceinline__ static int kof(int row, int col) { return KROWS ? row : col; }
+  __device__ __forceinline__ static int mnof(int row, int col) { return KROWS ? col : row; }
+};
+
+// TA / TB: A / B are stored transposed (op(A) = A^T, op(B) = B^T).
+// VA / VB: A / B take 16-byte loads.  KFULL: K % BK == 0.
 template <int BM, int BN, int BK, int WM, int WN, bool SWZ, bool KFULL, int SCHED, bool VA,
-          bool VB>
+          bool VB, bool TA, bool TB>
 __global__ void __launch_bounds__(WM *WN *kWave)
 mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int KH = BK / 2, G = KH / 4;
-  // Each lane of a load moves EA (EB) floats; a block of one wave-wide load
-  // covers 64*EA (64*EB) consecutive floats of the LDS image.
-  constexpr int EA = VA ? 4 : 1, EB = VB ? 4 : 1;
-  constexpr int FPB_A = kWave * EA, FPB_B = kWave * EB;
-  constexpr int DA = BM * BK / FPB_A, DB = BK * BN / FPB_B;  // blocks per slice
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(G >= 2, "BK must be 16 or 32");
-  static_assert(DA % NW == 0 && DB % NW == 0, "blocks must split evenly over the waves");
-  constexpr int DAW = DA / NW, DBW = DB / NW;
+  // A as given has k along its columns; transposed, along its rows.  B the
+  // other way round.
+  using GA = SliceGeom<BM, BK, TA, VA, SWZ, NW>;
+  using GB = SliceGeom<BN, BK, !TB, VB, SWZ, NW>;
 
   __shared__ __attribute__((aligned(1024))) float As0[BM * BK];
   __shared__ __attribute__((aligned(1024))) float As1[BM * BK];
@@ -115,43 +152,32 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   const int wm = wave / WN, wn = wave % WN;
   const int r32 = lane % 32, half = lane / 32;
 
+  // Launch position -> (product of the batch, tile).
+  const int tiles = tiles_m * tiles_n;
+  const int id = xcd_contiguous_id(blockIdx.x, gridDim.x);
+  const int bidx = id / tiles;
   int tm, tn;
-  grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
+  grouped_tile(id - bidx * tiles, tiles_m, tiles_n, group_m, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
+  const float *Ab = p.A + (long)bidx * p.strideA;
+  const float *Bb = p.B + (long)bidx * p.strideB;
+  float *Cb = p.C + (long)bidx * p.strideC;
 
-  // Slice element fetched by this lane in the wave's q-th block: row and
-  // column within the slice (A: row of the m tile, k; B: k, column of the n
-  // tile).  The LDS image is A row-major with its 16-byte chunks swizzled,
-  // B row-major; a lane's LDS position is fixed, so it fetches whichever
-  // element belongs there.
-  auto a_elem = [&](int q, int &row, int &k) {
-    const int f = (wave + q * NW) * FPB_A + lane * EA;  // LDS position in the slice
-    row = f / BK;
-    const int pc = f % BK;
-    k = 4 * ((pc / 4) ^ a_swizzle<BK, SWZ>(row)) + pc % 4;
-  };
-  auto b_elem = [&](int q, int &row, int &c) {
-    const int f = (wave + q * NW) * FPB_B + lane * EB;
-    row = f / BN;
-    c = f % BN;
-  };
-
-  // Per-lane byte offsets relative to the slice origin (row m0 / column k0
-  // of A; row k0 / column n0 of B).  Elements in rows of A past M or columns
-  // of B past N get the out-of-range offset once and for all; the K tail is
-  // handled per slice.
-  unsigned offA[DAW], offB[DBW];
+  // Per-lane byte offsets relative to the slice origin.  Elements outside
+  // op(A)'s rows (M) or op(B)'s columns (N) get the out-of-range offset once
+  // and for all; the K tail is handled per slice.
+  unsigned offA[GA::NBW], offB[GB::NBW];
 #pragma unroll
-  for (int q = 0; q < DAW; ++q) {
-    int row, k;
-    a_elem(q, row, k);
-    offA[q] = m0 + row < p.M ? (unsigned)(row * p.lda + k) * 4u : kOutOfRange;
+  for (int q = 0; q < GA::NBW; ++q) {
+    int row, col;
+    GA::elem(wave, lane, q, row, col);
+    offA[q] = m0 + GA::mnof(row, col) < p.M ? (unsigned)(row * p.lda + col) * 4u : kOutOfRange;
   }
 #pragma unroll
-  for (int q = 0; q < DBW; ++q) {
-    int row, c;
-    b_elem(q, row, c);
-    offB[q] = n0 + c < p.N ? (unsigned)(row * p.ldb + c) * 4u : kOutOfRange;
+  for (int q = 0; q < GB::NBW; ++q) {
+    int row, col;
+    GB::elem(wave, lane, q, row, col);
+    offB[q] = n0 + GB::mnof(row, col) < p.N ? (unsigned)(row * p.ldb + col) * 4u : kOutOfRange;
   }
 
   // Issue the loads of slice t into LDS stage S.  A slice at or past the end
@@ -163,43 +189,47 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   auto dma = [&](auto S, int t) {
     float *as = S.value ? As1 : As0;
     float *bs = S.value ? Bs1 : Bs0;
-    const int k0 = t * BK;
+    const int k0 = t < nk ? t * BK : 0;
     const int records = t < nk ? kBufferRecords : 0;
+    const float *abase = TA ? Ab + (long)k0 * p.lda + m0 : Ab + (long)m0 * p.lda + k0;
+    const float *bbase = TB ? Bb + (long)n0 * p.ldb + k0 : Bb + (long)k0 * p.ldb + n0;
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(p.A + (long)m0 * p.lda + (t < nk ? k0 : 0)), 0, records,
-        kRawBufferWord3);
+        const_cast<float *>(abase), 0, records, kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(p.B + (long)(t < nk ? k0 : 0) * p.ldb + n0), 0, records,
-        kRawBufferWord3);
+        const_cast<float *>(bbase), 0, records, kRawBufferWord3);
 #pragma unroll
-    for (int q = 0; q < DAW; ++q) {
+    for (int q = 0; q < GA::NBW; ++q) {
       unsigned off = offA[q];
       if constexpr (!KFULL) {
-        int row, k;
-        a_elem(q, row, k);
-        off = k0 + k < p.K ? off : kOutOfRange;
+        int row, col;
+        GA::elem(wave, lane, q, row, col);
+        off = k0 + GA::kof(row, col) < p.K ? off : kOutOfRange;
       }
-      lds_dma<VA>(ra, as + (wave + q * NW) * FPB_A, off);
+      lds_dma<VA>(ra, as + (wave + q * NW) * GA::FPB, off);
     }
 #pragma unroll
-    for (int q = 0; q < DBW; ++q) {
+    for (int q = 0; q < GB::NBW; ++q) {
       unsigned off = offB[q];
       if constexpr (!KFULL) {
-        int row, c;
-        b_elem(q, row, c);
-        off = k0 + row < p.K ? off : kOutOfRange;
+        int row, col;
+        GB::elem(wave, lane, q, row, col);
+        off = k0 + GB::kof(row, col) < p.K ? off : kOutOfRange;
       }
-      lds_dma<VB>(rb, bs + (wave + q * NW) * FPB_B, off);
+      lds_dma<VB>(rb, bs + (wave + q * NW) * GB::FPB, off);
     }
   };
 
-  // Operand read offsets (floats).  Row wm*WTM + i*32 + r32 of the A slice
-  // has swizzle a_swizzle(r32), the same for every i.
-  const int sw = a_swizzle<BK, SWZ>(r32);
-  int a_off[G];
+  // Operand read offsets (floats).  In a k-contiguous image, row
+  // base + i*32 + r32 (base a multiple of 32) has swizzle kc_swizzle(r32).
+  const int sw = kc_swizzle<BK, SWZ>(r32);
+  int a_off[G], b_off[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) a_off[g] = (wm * WTM + r32) * BK + 4 * ((half * (KH / 4) + g) ^ sw);
-  const int b_off = half * KH * BN + wn * WTN + r32;
+  for (int g = 0; g < G; ++g) {
+    a_off[g] = TA ? (half * KH + g * 4) * BM + wm * WTM + r32
+                  : (wm * WTM + r32) * BK + 4 * ((half * (KH / 4) + g) ^ sw);
+    b_off[g] = TB ? (wn * WTN + r32) * BK + 4 * ((half * (KH / 4) + g) ^ sw)
+                  : (half * KH + g * 4) * BN + wn * WTN + r32;
+  }
 
   struct Ops {
     f32x4 a[FM];
@@ -209,12 +239,23 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     const float *as = S.value ? As1 : As0;
     const float *bs = S.value ? Bs1 : Bs0;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      o.a[i] = *reinterpret_cast<const f32x4 *>(as + a_off[g] + i * 32 * BK);
+    for (int i = 0; i < FM; ++i) {
+      if constexpr (TA) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+        for (int t = 0; t < 4; ++t) o.a[i][t] = as[a_off[g] + t * BM + i * 32];
+      } else {
+        o.a[i] = *reinterpret_cast<const f32x4 *>(as + a_off[g] + i * 32 * BK);
+      }
+    }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) o.b[j][t] = bs[b_off + (g * 4 + t) * BN + j * 32];
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (TB) {
+        o.b[j] = *reinterpret_cast<const f32x4 *>(bs + b_off[g] + j * 32 * BK);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o.b[j][t] = bs[b_off[g] + t * BN + j * 32];
+      }
+    }
   };
 
   f32x16 acc[FM][FN];
@@ -238,15 +279,14 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   using S1 = std::integral_constant<int, 1>;
   Ops cur, nxt;
 
-  // Instruction interleaving inside one group (SCHED = 1): after every two
-  // matrix-core instructions, one of the group's LDS reads (and, in the last
-  // group, first one buffer-to-LDS load per instruction), so that neither
-  // burst leaves the matrix pipe idle.
+  // Instruction interleaving inside one group (SCHED = 1): first one
+  // matrix-core instruction per buffer-to-LDS load (last group only), then
+  // two per LDS read, so that neither burst leaves the matrix pipe idle.
   constexpr int NMFMA = 4 * FM * FN;
-  constexpr int NDS = FM + 2 * FN;  // 128-bit A reads + paired 32-bit B reads
+  constexpr int NDS = (TA ? 2 * FM : FM) + (TB ? FN : 2 * FN);  // 128-bit or paired 32-bit reads
   auto interleave = [&](auto with_dma) {
     if constexpr (SCHED == 1) {
-      constexpr int nv = decltype(with_dma)::value ? DAW + DBW : 0;
+      constexpr int nv = decltype(with_dma)::value ? GA::NBW + GB::NBW : 0;
 #pragma unroll
       for (int q = 0; q < nv; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // matrix core
@@ -262,6 +302,8 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     }
   };
 
+  // Slice t lives in stage S; slice t+1 (if any) is already on its way to
+  // stage S^1.
   auto slice = [&](auto S, int t) {
     constexpr int s = decltype(S)::value;
     using SN = std::integral_constant<int, s ^ 1>;
@@ -295,51 +337,97 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   // let them retire before the work-group gives up its LDS.
   __builtin_amdgcn_s_waitcnt(0x0f70);
 
+  // Epilogue: register e of lane l holds row acc32_row(l, e), column l % 32
+  // of its 32x32 block; rows >= M and columns >= N are not stored.  C is read
+  // only when beta != 0, and then a block's 16 values per lane are all loaded
+  // before any of them is stored (a store could alias a later load, so the
+  // compiler would otherwise wait out each load's latency in turn).
   const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN + r32;
   const bool full = (m0 + BM <= p.M) && (n0 + BN <= p.N);
+  const bool plain = p.alpha == 1.f && p.beta == 0.f;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int j = 0; j < FN; ++j) {
+      const int col = col0 + j * 32;
+      auto row = [&](int e) { return row0 + i * 32 + acc32_row(lane, e); };
+      auto inside = [&](int e) { return full || (row(e) < p.M && col < p.N); };
+      auto at = [&](int e) { return Cb + (long)row(e) * p.ldc + col; };
+      if (plain) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = row0 + i * 32 + acc32_row(lane, e);
-        const int col = col0 + j * 32;
-        if (full || (row < p.M && col < p.N)) p.C[(long)row * p.ldc + col] = acc[i][j][e];
+        for (int e = 0; e < 16; ++e)
+          if (inside(e)) *at(e) = acc[i][j][e];
+      } else if (p.beta == 0.f) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (inside(e)) *at(e) = p.alpha * acc[i][j][e];
+      } else {
+        float c[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) c[e] = inside(e) ? *at(e) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (inside(e)) *at(e) = fmaf(p.alpha, acc[i][j][e], p.beta * c[e]);
       }
+    }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool SWZ, int SCHED, bool VA, bool VB>
+template <int BM, int BN, int BK, int WM, int WN, bool SWZ, int SCHED, bool VA, bool VB, bool TA,
+          bool TB>
 inline void launch_dma_kernel(const GemmArgs &p, hipStream_t stream, int group_m) {
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-  const dim3 grid((unsigned)((long)tiles_m * tiles_n)), block(WM * WN * kWave);
+  const dim3 grid((unsigned)((long)tiles_m * tiles_n * p.batch)), block(WM * WN * kWave);
   if (p.K % BK == 0)
-    hipLaunchKernelGGL((mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, true, SCHED, VA, VB>), grid,
-                       block, 0, stream, p, tiles_m, tiles_n, group_m);
+    hipLaunchKernelGGL(
+        (mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, true, SCHED, VA, VB, TA, TB>), grid,
+        block, 0, stream, p, tiles_m, tiles_n, group_m);
   else
-    hipLaunchKernelGGL((mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, false, SCHED, VA, VB>),
-                       grid, block, 0, stream, p, tiles_m, tiles_n, group_m);
+    hipLaunchKernelGGL(
+        (mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, false, SCHED, VA, VB, TA, TB>), grid,
+        block, 0, stream, p, tiles_m, tiles_n, group_m);
 }
 
-// WIDE_ONLY instantiates only the 16-byte-load form; the caller guarantees
-// va && vb.
+template <int BM, int BN, int BK, int WM, int WN, bool SWZ, int SCHED, bool TA, bool TB>
+inline void launch_dma_widths(const GemmArgs &p, bool va, bool vb, hipStream_t stream,
+                              int group_m) {
+  if (va && vb)
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true, TA, TB>(p, stream, group_m);
+  else if (va)
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, false, TA, TB>(p, stream, group_m);
+  else if (vb)
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, true, TA, TB>(p, stream, group_m);
+  else
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, false, TA, TB>(p, stream, group_m);
+}
+
+// Plain layout (no transposes).  WIDE_ONLY instantiates only the 16-byte-load
+// form; the caller guarantees va && vb.
 template <int BM, int BN, int BK, int WM, int WN, bool SWZ = true, int SCHED = 1,
           bool WIDE_ONLY = false>
 inline hipError_t launch_dma_cfg(const GemmArgs &p, bool va, bool vb, hipStream_t stream,
                                  int group_m = 8) {
   if constexpr (WIDE_ONLY) {
     if (!(va && vb)) return hipErrorInvalidValue;
-    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true>(p, stream, group_m);
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true, false, false>(p, stream,
+                                                                                group_m);
   } else {
-    if (va && vb)
-      launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true>(p, stream, group_m);
-    else if (va)
-      launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, false>(p, stream, group_m);
-    else if (vb)
-      launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, true>(p, stream, group_m);
-    else
-      launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, false>(p, stream, group_m);
+    launch_dma_widths<BM, BN, BK, WM, WN, SWZ, SCHED, false, false>(p, va, vb, stream, group_m);
   }
+  return hipGetLastError();
+}
+
+// Any layout.
+template <int BM, int BN, int BK, int WM, int WN>
+inline hipError_t launch_dma_general(const GemmArgs &p, bool ta, bool tb, bool va, bool vb,
+                                     hipStream_t stream, int group_m = 8) {
+  if (!ta && !tb)
+    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, false, false>(p, va, vb, stream, group_m);
+  else if (!ta)
+    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, false, true>(p, va, vb, stream, group_m);
+  else if (!tb)
+    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, true, false>(p, va, vb, stream, group_m);
+  else
+    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, true, true>(p, va, vb, stream, group_m);
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ template <int BM, int BN, int BK, int WM, int WN, bool WIDE_ONLY = false>
 static hipError_t launch_tile(MfmaPath path, const GemmArgs &p, bool va, bool vb,
                               hipStream_t stream) {
   constexpr int kStoreGroup = 1;  // staged kernel: write the next slice after group 1 of 4
-  const bool dma = dma_offsets_fit(BM, BK, p.lda, p.ldb, BN);
+  const bool dma = dma_offsets_fit(BM, p.lda, BK, p.ldb);
   switch (path) {
     case MfmaPath::Auto:
       if (dma) return launch_dma_cfg<BM, BN, BK, WM, WN, true, 1, WIDE_ONLY>(p, va, vb, stream);
@@ -32,10 +32,16 @@ static hipError_t launch_tile(MfmaPath path, const GemmArgs &p, bool va, bool vb
   return hipErrorInvalidValue;
 }
 
-MfmaTile choose_mfma_tile(long M, long N, int cus) {
-  auto tiles = [&](long t) { return ((M + t - 1) / t) * ((N + t - 1) / t); };
-  if (tiles(256) >= cus) return MfmaTile::T256;
-  if (tiles(128) >= cus) return MfmaTile::T128;
+// The largest tile that still gives every compute unit a work-group and
+// whose tiles are at least 3/4 inside C (a 256 x 256 tile over a 64 x 64
+// product would compute 16 times the useful work); else the smallest.
+MfmaTile choose_mfma_tile(long M, long N, int cus, long batch) {
+  auto good = [&](long t) {
+    const long tm = (M + t - 1) / t, tn = (N + t - 1) / t;
+    return (double)tm * tn * batch >= cus && 4.0 * M * N >= 3.0 * tm * tn * t * t;
+  };
+  if (good(256)) return MfmaTile::T256;
+  if (good(128)) return MfmaTile::T128;
   return MfmaTile::T64;
 }
 
@@ -51,6 +57,25 @@ hipError_t launch_mfma(MfmaTile tile, MfmaPath path, const GemmArgs &p, bool va,
     case MfmaTile::T64: return launch_tile<64, 64, 32, 2, 2>(path, p, va, vb, stream);
   }
   return hipErrorInvalidValue;
+}
+
+template <int BM, int BN, int BK, int WM, int WN>
+static hipError_t launch_general_tile(const GemmArgs &p, bool ta, bool tb, bool va, bool vb,
+                                      hipStream_t stream) {
+  if (!dma_offsets_fit(ta ? BK : BM, p.lda, tb ? BN : BK, p.ldb)) return hipErrorInvalidValue;
+  return launch_dma_general<BM, BN, BK, WM, WN>(p, ta, tb, va, vb, stream);
+}
+
+hipError_t launch_mfma_general(MfmaTile tile, const GemmArgs &p, bool ta, bool tb, bool va,
+                               bool vb, hipStream_t stream) {
+  // The 256 x 256 tile is instantiated for the plain layout with 16-byte
+  // loads only (other forms would spill); the rest use 128 x 128.
+  if (tile == MfmaTile::T256 && !ta && !tb && va && vb) {
+    if (!dma_offsets_fit(256, p.lda, 32, p.ldb)) return hipErrorInvalidValue;
+    return launch_dma_cfg<256, 256, 32, 2, 4, true, 1, true>(p, va, vb, stream);
+  }
+  if (tile == MfmaTile::T64) return launch_general_tile<64, 64, 32, 2, 2>(p, ta, tb, va, vb, stream);
+  return launch_general_tile<128, 128, 32, 2, 2>(p, ta, tb, va, vb, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -191,22 +191,27 @@ hipError_t launch_valu(int rung, const GemmArgs &p, bool va, bool vb, hipStream_
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- K == 0
-__global__ void __launch_bounds__(256) zero_kernel(float *C, long ldc, int M, int N) {
-  const long total = (long)M * N;
+// ---------------------------------------------------------------- C = beta C
+// Over p.batch products: C = beta * C, or zeros when beta == 0 (C not read).
+// This is the whole product when K == 0 or alpha == 0.
+__global__ void __launch_bounds__(256) scale_kernel(GemmArgs p) {
+  const long per = (long)p.M * p.N;
+  const long total = per * p.batch;
   for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < total;
        q += (long)gridDim.x * blockDim.x) {
-    const long row = q / N, col = q % N;
-    C[row * ldc + col] = 0.f;
+    const long b = q / per, r = q % per;
+    const long row = r / p.N, col = r % p.N;
+    float *c = p.C + b * p.strideC + row * p.ldc + col;
+    *c = p.beta == 0.f ? 0.f : p.beta * *c;
   }
 }
 
-hipError_t launch_zero(const GemmArgs &p, hipStream_t stream) {
-  const long total = (long)p.M * p.N;
+hipError_t launch_scale(const GemmArgs &p, hipStream_t stream) {
+  const long total = (long)p.M * p.N * p.batch;
   long blocks = (total + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p.C, p.ldc, p.M,
-                     p.N);
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(scale_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

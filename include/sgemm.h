@@ -121,6 +121,45 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K,
                       float *C, int64_t ldc, void *stream);
 
 /*
+ * The general form: C = alpha * op(A) op(B) + beta * C, the plain product
+ * extended by the two steps around it.  The article "硬件加速原理：CUDA核函数
+ * 优化矩阵乘法的内存访问模式" (section "访问模式对比") contrasts row- and
+ * column-major operands; transposed operands are how a row-major interface
+ * takes column-major data.
+ *
+ * op(A) is M x K: A itself (transA == 0, stored M x K, lda >= max(1, K)) or
+ * the transpose of a stored K x M matrix (transA == 1, lda >= max(1, M),
+ * op(A)(i,k) = A[k*lda + i]).  op(B) is K x N: B itself (transB == 0, stored
+ * K x N, ldb >= max(1, N)) or the transpose of a stored N x K matrix
+ * (transB == 1, ldb >= max(1, K), op(B)(k,j) = B[j*ldb + k]).  C is M x N,
+ * ldc >= max(1, N).  When beta == 0, C is only written (NaN or Inf in it do
+ * not propagate); when alpha == 0 or K == 0, A and B are not read and
+ * C = beta * C.  Products are summed in single precision as in sgemm_run;
+ * the result is alpha * sum + beta * C, rounded once after beta * C.
+ * Returns SGEMM_ERR_TOO_LARGE, besides the cases of sgemm_run, when a
+ * leading dimension is so large that one K slice spans 2 GiB.
+ */
+int sgemm_run_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                 const float *A, int64_t lda, const float *B, int64_t ldb, float beta,
+                 float *C, int64_t ldc, void *stream);
+
+/*
+ * `batch` independent general products on one stream: product b uses
+ * A + b*strideA, B + b*strideB and C + b*strideC (strides in floats,
+ * >= 0; a stride of 0 shares that operand).  The C matrices of different
+ * products must not overlap: with batch > 1, strideC < (M - 1) * ldc + N is
+ * SGEMM_ERR_INVALID_VALUE.  Many small products in one launch fill the
+ * device where one alone cannot; batched matrix work is the subject that the
+ * address of the textbook chapter "4. 矩阵乘法性能优化" names.  batch == 0 is
+ * a no-op.
+ */
+int sgemm_run_strided_batched(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                              float alpha, const float *A, int64_t lda, int64_t strideA,
+                              const float *B, int64_t ldb, int64_t strideB, float beta,
+                              float *C, int64_t ldc, int64_t strideC, int64_t batch,
+                              void *stream);
+
+/*
  * Matrix-core layout probe: one wave multiplies a 32 x 2 block of A by a
  * 2 x 32 block of B (which = 0, v_mfma_f32_32x32x2_f32) or a 16 x 4 block by
  * a 4 x 16 block (which = 1, v_mfma_f32_16x16x4_f32), with A and B row-major

@@ -28,7 +28,7 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = set(_declared_functions())
     for n in ("sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_run_variant",
-              "sgemm_mfma_probe", "sgemm_status_string", "sgemm_variant_name"):
+              "sgemm_run_ex", "sgemm_run_strided_batched", "sgemm_mfma_probe", "sgemm_status_string", "sgemm_variant_name"):
         assert n in names
 
 
@@ -82,3 +82,39 @@ def test_unknown_variant_rejected():
 def test_destroy_without_create():
     lib = sg.load_library()
     assert sg.sgemm_status_string(lib.sgemm_destroy()) == "SGEMM_ERR_NOT_INITIALIZED"
+
+
+# (transA, transB, M, N, K, lda, ldb, ldc, strideA, strideB, strideC, batch), status
+@pytest.mark.parametrize("args,status", [
+    ((2, 0, 4, 4, 4, 4, 4, 4, 0, 0, 16, 1), "SGEMM_ERR_INVALID_VALUE"),   # bad transA
+    ((0, -1, 4, 4, 4, 4, 4, 4, 0, 0, 16, 1), "SGEMM_ERR_INVALID_VALUE"),  # bad transB
+    ((1, 0, 8, 4, 4, 4, 4, 4, 0, 0, 32, 1), "SGEMM_ERR_INVALID_VALUE"),   # transA: lda < M
+    ((0, 1, 4, 8, 6, 6, 4, 8, 0, 0, 32, 1), "SGEMM_ERR_INVALID_VALUE"),   # transB: ldb < K
+    ((0, 1, 4, 8, 6, 6, 6, 8, 0, 0, 32, 1), "SGEMM_ERR_NOT_INITIALIZED"),  # transB: ldb >= K
+    ((0, 0, 4, 4, 4, 4, 4, 4, -4, 0, 16, 2), "SGEMM_ERR_INVALID_VALUE"),  # negative stride
+    ((0, 0, 4, 4, 4, 4, 4, 4, 0, 0, 15, 2), "SGEMM_ERR_INVALID_VALUE"),   # C matrices overlap
+    ((0, 0, 4, 4, 4, 4, 4, 8, 0, 0, 28, 2), "SGEMM_ERR_NOT_INITIALIZED"),  # (M-1)ldc+N = 28
+    ((0, 0, 4, 4, 4, 4, 4, 4, 0, 0, 0, 1), "SGEMM_ERR_NOT_INITIALIZED"),  # one product
+    ((0, 0, 4, 4, 4, 4, 4, 4, 0, 0, 16, -1), "SGEMM_ERR_INVALID_VALUE"),  # negative batch
+    ((0, 0, 4, 4, 4, 4, 4, 4, 0, 0, 16, 2 ** 31), "SGEMM_ERR_TOO_LARGE"),
+])
+def test_general_host_side_argument_checks(args, status):
+    lib = sg.load_library()
+    ta, tb, M, N, K, lda, ldb, ldc, sA, sB, sC, batch = args
+    rc = lib.sgemm_run_strided_batched(ta, tb, M, N, K, 1.0, 1, lda, sA, 1, ldb, sB, 0.0, 1, ldc,
+                                       sC, batch, None)
+    assert sg.sgemm_status_string(rc) == status
+    if batch == 1:
+        rc = lib.sgemm_run_ex(ta, tb, M, N, K, 1.0, 1, lda, 1, ldb, 0.0, 1, ldc, None)
+        assert sg.sgemm_status_string(rc) == status
+
+
+def test_general_null_operands():
+    lib = sg.load_library()
+    # alpha == 0: A and B are not read, so they may be NULL
+    rc = lib.sgemm_run_ex(0, 0, 4, 4, 4, 0.0, None, 4, None, 4, 1.0, 1, 4, None)
+    assert sg.sgemm_status_string(rc) == "SGEMM_ERR_NOT_INITIALIZED"
+    rc = lib.sgemm_run_ex(0, 0, 4, 4, 4, 1.0, None, 4, 1, 4, 1.0, 1, 4, None)
+    assert sg.sgemm_status_string(rc) == "SGEMM_ERR_INVALID_VALUE"
+    rc = lib.sgemm_run_ex(0, 0, 4, 4, 4, 1.0, 1, 4, 1, 4, 1.0, None, 4, None)
+    assert sg.sgemm_status_string(rc) == "SGEMM_ERR_INVALID_VALUE"
