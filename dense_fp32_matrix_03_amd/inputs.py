@@ -142,3 +142,22 @@ def sign_vector(n: int, seed: int) -> np.ndarray:
     """A +-1 probe vector for the whole-matrix (Freivalds) check."""
     g = np.random.default_rng(20_000 + seed)
     return np.where(g.random(n) < 0.5, -1.0, 1.0)
+
+
+# Vector addition (the blog's experiment 1): n = 2^24 floats, A[i] = sin(i)^2
+# and B[i] = cos(i)^2 with i converted to float and single-precision sine and
+# cosine, so every exact sum is close to 1.
+VECTOR_ADD_N = 1 << 24
+
+
+def vector_add_inputs(n: int = VECTOR_ADD_N, kind: str = "sincos", seed: int = 0):
+    """Return (A, B), float32 arrays of n elements."""
+    if kind == "sincos":
+        x = np.arange(n, dtype=np.float32)
+        s = np.sin(x)
+        c = np.cos(x)
+        return (s * s).astype(np.float32), (c * c).astype(np.float32)
+    if kind == "uniform":
+        g = np.random.default_rng(seed)
+        return uniform(g, (n,)), uniform(g, (n,))
+    raise ValueError(f"unknown vector-add input kind {kind!r}")

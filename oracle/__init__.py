@@ -20,6 +20,8 @@ What is here:
   sizes where the full oracle product is too slow: for a sign vector x,
   |(C x)_i - (A (B x))_i| <= 1e-5 (|A| (|B| |x|))_i + 1e-6 N.
 * ``exact_products`` -- exact rational sums for tiny inputs (brute force).
+* ``vector_add`` -- C[i] = A[i] + B[i] correctly rounded to float (the
+  blog's experiment 1, "向量加法"), from ``oracle_vector_add`` in oracle.c.
 
 Matrices are passed as numpy float32 arrays of shape (rows, ld); the logical
 column count is given separately, so columns ld > cols are padding that the
@@ -74,6 +76,8 @@ def _load():
                                         ctypes.c_double, fp, i64, fp, i64, ctypes.c_double,
                                         fp, i64, dp, i64, dp, i64, ctypes.c_int]
     lib.oracle_sgemm_ex_f64.restype = ctypes.c_int
+    lib.oracle_vector_add.argtypes = [i64, fp, fp, fp]
+    lib.oracle_vector_add.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -252,3 +256,19 @@ def exact_products(A: np.ndarray, B: np.ndarray) -> list:
     FB = [[Fraction(float(B[k, j])) for j in range(N)] for k in range(K)]
     return [[sum((FA[i][k] * FB[k][j] for k in range(K)), Fraction(0)) for j in range(N)]
             for i in range(M)]
+
+
+def vector_add(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """C = A + B elementwise for 1-D float32 arrays, each sum correctly
+    rounded to float32."""
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    if A.dtype != np.float32 or B.dtype != np.float32:
+        raise TypeError("A and B must be float32")
+    if A.ndim != 1 or A.shape != B.shape:
+        raise ValueError(f"shapes {A.shape} and {B.shape} must be equal and 1-D")
+    C = np.empty_like(A)
+    rc = _load().oracle_vector_add(A.shape[0], _ptr(A), _ptr(B), _ptr(C))
+    if rc != 0:
+        raise ValueError(f"oracle_vector_add rejected its arguments (rc={rc})")
+    return C

@@ -176,6 +176,26 @@ int oracle_sgemm_ex_f64(int transA, int transB, int64_t M, int64_t N, int64_t K,
     return ORACLE_OK;
 }
 
+/*
+ * Vector addition C[i] = A[i] + B[i], i = 0 .. n-1, in single precision
+ * [blog "【infra之路】03_动手写 CUDA Kernel", 实验 1 (experiment 1), the
+ * vector-addition kernel: one element per thread, one add].  The result is
+ * the correctly rounded (round-to-nearest-even) float sum: the sum is formed
+ * in double and rounded once to float, and since double carries more than
+ * 2 * 24 + 2 significand bits, rounding first to double and then to float
+ * gives the same float as rounding the exact sum directly (the classical
+ * double-rounding result for +, -, x, / and square root).  Returns
+ * ORACLE_BAD_ARG for n < 0 or a null pointer with n > 0.
+ */
+int oracle_vector_add(int64_t n, const float *A, const float *B, float *C)
+{
+    if (n < 0 || (n > 0 && (!A || !B || !C)))
+        return ORACLE_BAD_ARG;
+    for (int64_t i = 0; i < n; ++i)
+        C[i] = (float)((double)A[i] + (double)B[i]);
+    return ORACLE_OK;
+}
+
 /* Threads OpenMP would use by default; 1 when built without OpenMP. */
 int oracle_max_threads(void)
 {

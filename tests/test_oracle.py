@@ -14,6 +14,8 @@ as a width) fails at least one of them:
 """
 import os
 
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -359,3 +361,74 @@ def test_pins_catch_a_wrong_transpose_flag():
     right, _ = oracle.sgemm_ex_f64(False, False, 6, 6, 6, 1.0, A, B)
     wrong, _ = oracle.sgemm_ex_f64(True, False, 6, 6, 6, 1.0, A, B)
     assert not np.array_equal(right, wrong)
+
+
+# ---------------------------------------------------------------- vector add
+# Pins of oracle.vector_add: the blog's own check (sin^2 + cos^2 = 1, experiment
+# 1), correct rounding against exact rationals, and IEEE special cases.
+
+def _rne_ok(a, b, c) -> bool:
+    """c is the float32 nearest to the exact a + b, ties to even."""
+    a, b, c = np.float32(a), np.float32(b), np.float32(c)
+    if not np.isfinite(c):
+        return False
+    exact = Fraction(float(a)) + Fraction(float(b))
+    d = abs(Fraction(float(c)) - exact)
+    for nb in (np.nextafter(c, np.float32(np.inf)), np.nextafter(c, np.float32(-np.inf))):
+        if not np.isfinite(nb):
+            continue
+        dn = abs(Fraction(float(nb)) - exact)
+        if dn < d:
+            return False
+        if dn == d and (int(c.view(np.uint32)) & 1):
+            return False  # a tie must go to the even neighbour
+    return True
+
+
+def test_vector_add_sin_cos_identity_at_full_size():
+    """The blog checks max |C[i] - 1| for A = sin^2(i), B = cos^2(i), n = 2^24.
+    Each input carries at most a few float32 roundings of a value <= 1, so
+    the sum is within 8 units of 2^-24 of 1."""
+    A, B = inputs.vector_add_inputs()
+    assert A.shape == (1 << 24,)
+    C = oracle.vector_add(A, B)
+    assert float(np.max(np.abs(C.astype(np.float64) - 1.0))) <= 8 * 2.0 ** -24
+
+
+def test_vector_add_correct_rounding_brute_force():
+    g = np.random.default_rng(4242)
+    a = (g.standard_normal(3000) * np.exp2(g.integers(-30, 30, 3000))).astype(np.float32)
+    b = (g.standard_normal(3000) * np.exp2(g.integers(-30, 30, 3000))).astype(np.float32)
+    # ties: 1 + 2^-24 rounds down to 1, (1 + 2^-23) + 2^-24 rounds up to 1 + 2^-22
+    a = np.concatenate([a, np.float32([1.0, 1.0 + 2.0 ** -23, 3.0, -1.0])])
+    b = np.concatenate([b, np.float32([2.0 ** -24, 2.0 ** -24, 2.0 ** -23, -2.0 ** -24])])
+    c = oracle.vector_add(a, b)
+    bad = [i for i in range(a.shape[0]) if not _rne_ok(a[i], b[i], c[i])]
+    assert not bad, [(a[i], b[i], c[i]) for i in bad[:5]]
+    assert c[-4] == np.float32(1.0) and c[-3] == np.float32(1.0 + 2.0 ** -22)
+
+
+def test_vector_add_rounding_check_catches_wrong_rounding():
+    """A planted round-up of a tie, and a truncated sum, must be rejected."""
+    assert not _rne_ok(1.0, 2.0 ** -24, 1.0 + 2.0 ** -23)
+    a, b = np.float32(1.0), np.float32(3 * 2.0 ** -25)  # exact 1 + 1.5 * 2^-24
+    assert _rne_ok(a, b, 1.0 + 2.0 ** -23) and not _rne_ok(a, b, 1.0)
+
+
+def test_vector_add_special_values():
+    big = np.finfo(np.float32).max
+    tiny = np.uint32(1).view(np.float32)  # smallest subnormal, 2^-149
+    a = np.float32([2.5, -7.0, 0.0, big, np.nan, -0.0, tiny])
+    b = np.float32([-2.5, 0.0, -0.0, big, 1.0, -0.0, tiny])
+    c = oracle.vector_add(a, b)
+    assert c[0] == 0.0 and not np.signbit(c[0])      # x + (-x) = +0
+    assert c[1] == -7.0                               # x + 0 = x
+    assert c[2] == 0.0 and not np.signbit(c[2])      # 0 + (-0) = +0
+    assert np.isposinf(c[3])                          # overflow
+    assert np.isnan(c[4])                             # NaN propagates
+    assert c[5] == 0.0 and np.signbit(c[5])          # -0 + -0 = -0
+    assert c[6].view(np.uint32) == 2                  # subnormals are kept
+    assert np.array_equal(oracle.vector_add(b, a)[:4], c[:4])
+    assert oracle.vector_add(np.zeros(0, np.float32), np.zeros(0, np.float32)).shape == (0,)
+    with pytest.raises(ValueError):
+        oracle.vector_add(np.zeros(3, np.float32), np.zeros(4, np.float32))
