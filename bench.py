@@ -264,6 +264,68 @@ def general_table(settle: float) -> list[dict]:
     return rows
 
 
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def vector_add_table(steps: int, settle: float) -> list[dict]:
+    """Effective bandwidth of vector_add, 3 * 4 * n bytes per call (A and B
+    read, C written), as the blog counts it.  "resident": the same three
+    arrays every call (at n = 2^24 they fit the 256 MB Infinity Cache, so
+    this can exceed HBM); "rotating": four sets of arrays used in turn, so
+    each call's operands were last touched four calls ago."""
+    import torch
+
+    import dense_fp32_matrix_03_amd as sg
+    from dense_fp32_matrix_03_amd import inputs
+
+    rows = []
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    for n, mode in ((inputs.VECTOR_ADD_N, "resident"), (inputs.VECTOR_ADD_N, "rotating"),
+                    (1 << 28, "resident")):
+        nsets = 4 if mode == "rotating" else 1
+        if n == inputs.VECTOR_ADD_N:
+            A, B = inputs.vector_add_inputs(n)
+        else:
+            A, B = inputs.vector_add_inputs(n, "uniform", seed=1)
+        sets = [(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(),
+                 torch.empty(n, dtype=torch.float32, device="cuda")) for _ in range(nsets)]
+        del A, B
+        calls = [0]
+
+        def step():
+            a, b, c = sets[calls[0] % nsets]
+            calls[0] += 1
+            sg.vector_add(n, a, b, c, h)
+
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+        t_end = time.perf_counter() + settle
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                step()
+            torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps):
+            step()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        gbs = 12.0 * n / (ms * 1e-3) / 1e9
+        ok = bool(torch.isfinite(sets[0][2]).all().item())
+        r = {"kernel": "vector_add", "n": n, "mode": mode, "sets": nsets, "steps": steps,
+             "us": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
+             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "output_finite": ok}
+        print(json.dumps(r), flush=True)
+        rows.append(r)
+        del sets
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description="single-precision GEMM throughput on MI355X")
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +347,9 @@ def main(argv=None) -> int:
     ap.add_argument("--general", action="store_true",
                     help="time the general form (transposes, alpha/beta, strided batches) "
                          "on a fixed set of cases, one JSON line each")
+    ap.add_argument("--vector-add", action="store_true",
+                    help="time vector_add (n = 2^24 with resident and rotating arrays, "
+                         "n = 2^28) and print its effective bandwidth, one JSON line each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -319,6 +384,10 @@ def main(argv=None) -> int:
     variant = sg.VARIANTS[a.variant] if a.variant in sg.VARIANTS else int(a.variant)
     if a.table:
         workload_table(variant)
+        sg.sgemm_destroy()
+        return 0
+    if a.vector_add:
+        vector_add_table(a.steps, a.settle)
         sg.sgemm_destroy()
         return 0
     if a.general:

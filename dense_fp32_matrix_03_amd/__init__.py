@@ -71,6 +71,8 @@ def load_library(path: str = LIB_PATH):
     lib.sgemm_run_strided_batched.argtypes = [ci, ci, i64, i64, i64, f32, vp, i64, i64, vp, i64,
                                               i64, f32, vp, i64, i64, i64, vp]
     lib.sgemm_run_strided_batched.restype = ci
+    lib.vector_add.argtypes = [i64, vp, vp, vp, vp]
+    lib.vector_add.restype = ci
     lib.sgemm_mfma_probe.argtypes = [ci, vp, vp, vp, vp]
     lib.sgemm_mfma_probe.restype = ci
     lib.sgemm_status_string.argtypes = [ci]
@@ -142,6 +144,12 @@ def sgemm_run_strided_batched(transA, transB, M, N, K, alpha, A, lda, strideA, B
     _check("sgemm_run_strided_batched", load_library().sgemm_run_strided_batched(
         int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda, strideA, _ptr(B), ldb,
         strideB, float(beta), _ptr(C), ldc, strideC, batch, _stream(stream)))
+
+
+def vector_add(n, A, B, C, stream=None) -> None:
+    """C[i] = A[i] + B[i] for i < n (include/vector_add.h)."""
+    _check("vector_add", load_library().vector_add(n, _ptr(A), _ptr(B), _ptr(C),
+                                                   _stream(stream)))
 
 
 def sgemm_mfma_probe(which, A, B, C, stream=None) -> None:

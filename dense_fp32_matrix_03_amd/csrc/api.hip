@@ -1,5 +1,6 @@
-// api.hip -- the C interface declared in include/sgemm.h: argument checks,
-// device check, and the choice of kernel configuration for each call.
+// api.hip -- the C interface declared in include/sgemm.h and
+// include/vector_add.h: argument checks, device check, and the choice of
+// kernel configuration for each call.
 #include <stdint.h>
 
 #include <atomic>
@@ -8,6 +9,7 @@
 
 #include "dispatch.hpp"
 #include "sgemm.h"
+#include "vector_add.h"
 
 namespace {
 
@@ -47,6 +49,17 @@ int current_device_info(DeviceInfo *out) {
 }
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+// A launch's work-items (work-groups x threads) must fit 32 bits.
+constexpr int64_t kMaxWorkItems = (int64_t(1) << 32) - 1;
+
+// Whether `batch` products of M x N, one `threads`-wide work-group per
+// tile x tile block of C, fit one launch.  The matrix-core kernels use at
+// most 256 threads per 64 x 64 block; the vector-FMA rungs 256 threads per
+// 16 x 16 block (or the equivalent).
+bool grid_fits(int64_t M, int64_t N, int64_t batch, int64_t tile, int64_t threads) {
+  const int64_t tiles = ((M + tile - 1) / tile) * ((N + tile - 1) / tile);
+  return batch == 0 || tiles <= kMaxWorkItems / threads / batch;
+}
 
 // Shared argument checks of every product entry point.
 int check_args(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
@@ -55,8 +68,7 @@ int check_args(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, con
   if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
     return SGEMM_ERR_INVALID_VALUE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return SGEMM_ERR_TOO_LARGE;
-  // One work-group per 16 x 16 tile must still fit a 32-bit grid.
-  if (((M + 15) / 16) * ((N + 15) / 16) > kMaxDim) return SGEMM_ERR_TOO_LARGE;
+  if (!grid_fits(M, N, 1, 64, 256)) return SGEMM_ERR_TOO_LARGE;
   if (M == 0 || N == 0) return SGEMM_OK;
   if (!C) return SGEMM_ERR_INVALID_VALUE;
   if (K > 0 && (!A || !B)) return SGEMM_ERR_INVALID_VALUE;
@@ -92,6 +104,7 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
   if (variant < 0 || variant >= SGEMM_NUM_VARIANTS) return SGEMM_ERR_INVALID_VALUE;
   int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc);
   if (rc != SGEMM_OK) return rc;
+  if (variant <= SGEMM_VARIANT_DBUF && !grid_fits(M, N, 1, 16, 256)) return SGEMM_ERR_TOO_LARGE;
   if (!g_ready.load(std::memory_order_acquire)) return SGEMM_ERR_NOT_INITIALIZED;
   if (M == 0 || N == 0) return SGEMM_OK;
   DeviceInfo di;
@@ -170,7 +183,7 @@ int sgemm_run_strided_batched(int transA, int transB, int64_t M, int64_t N, int6
       ldc < (N > 1 ? N : 1))
     return SGEMM_ERR_INVALID_VALUE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim || batch > kMaxDim) return SGEMM_ERR_TOO_LARGE;
-  if (batch > 0 && ((M + 15) / 16) * ((N + 15) / 16) > kMaxDim / batch) return SGEMM_ERR_TOO_LARGE;
+  if (!grid_fits(M, N, batch, 64, 256)) return SGEMM_ERR_TOO_LARGE;
   const bool reads_ab = K > 0 && alpha != 0.f;
   if (M > 0 && N > 0 && batch > 0) {
     if (!C) return SGEMM_ERR_INVALID_VALUE;
@@ -230,6 +243,19 @@ int sgemm_mfma_probe(int which, const float *A, const float *B, float *C, void *
   if (rc != SGEMM_OK) return rc;
   const hipError_t err =
       sgemm::launch_mfma_probe(which, A, B, C, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+int vector_add(int64_t n, const float *A, const float *B, float *C, void *stream) {
+  if (n < 0 || (n > 0 && (!A || !B || !C))) return SGEMM_ERR_INVALID_VALUE;
+  if (n > (int64_t(1) << 33)) return SGEMM_ERR_TOO_LARGE;
+  if (!g_ready.load(std::memory_order_acquire)) return SGEMM_ERR_NOT_INITIALIZED;
+  if (n == 0) return SGEMM_OK;
+  DeviceInfo di;
+  const int rc = current_device_info(&di);
+  if (rc != SGEMM_OK) return rc;
+  const hipError_t err =
+      sgemm::launch_vector_add(n, A, B, C, reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 

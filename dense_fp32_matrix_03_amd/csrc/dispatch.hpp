@@ -44,5 +44,8 @@ hipError_t launch_mfma_probe(int which, const float *A, const float *B, float *C
 // 3 register-tiled with a double-buffered LDS pipeline.
 hipError_t launch_valu(int rung, const GemmArgs &p, bool va, bool vb, hipStream_t stream);
 
+// C[i] = A[i] + B[i], i < n (n >= 1).
+hipError_t launch_vector_add(long n, const float *A, const float *B, float *C,
+                             hipStream_t stream);
 
 }  // namespace sgemm

@@ -7,8 +7,9 @@
  * k of A(i,k) * B(k,j).  Definition: article "硬件加速原理：CUDA核函数优化矩阵
  * 乘法的内存访问模式", section "矩阵乘法的计算特性" (the summation formula), and
  * the opening paragraph of the textbook chapter "4. 矩阵乘法性能优化".  The
- * pages' kernels overwrite C with the sum and never read it; so does this
- * library: there is no alpha or beta.
+ * pages' kernels overwrite C with the sum and never read it; so do
+ * sgemm_run and sgemm_run_variant.  sgemm_run_ex and sgemm_run_strided_batched
+ * (below) add the general form alpha * op(A) op(B) + beta * C.
  *
  * Layout.  Element (i, k) of A is A[i*lda + k]; element (k, j) of B is
  * B[k*ldb + j]; element (i, j) of C is C[i*ldc + j] (the row-major indexing
@@ -40,6 +41,9 @@
  * Argument errors (SGEMM_ERR_INVALID_VALUE, SGEMM_ERR_TOO_LARGE) are found
  * before the library or the HIP runtime is consulted, so they are reported
  * even before sgemm_create.  sgemm_status_string() names each status.
+ * Limits (SGEMM_ERR_TOO_LARGE): M, N, K and batch below 2^31, and one launch
+ * below 2^32 work-items -- 256 per 64 x 64 block of C for the matrix-core
+ * kernels, 256 per 16 x 16 block for the vector-FMA variants.
  *
  * Threads.  sgemm_create / sgemm_destroy are serialised internally;
  * sgemm_run may be called from any thread once sgemm_create has succeeded.
@@ -59,7 +63,7 @@ extern "C" {
 #define SGEMM_ERR_UNSUPPORTED_DEVICE (-3) /* current device is not gfx950 */
 #define SGEMM_ERR_HIP (-4)              /* a HIP runtime query failed */
 #define SGEMM_ERR_LAUNCH (-5)           /* the runtime rejected a kernel launch */
-#define SGEMM_ERR_TOO_LARGE (-6)        /* a dimension is 2^31 or more */
+#define SGEMM_ERR_TOO_LARGE (-6)        /* a size is past the library's limits */
 
 /*
  * Kernel variants for sgemm_run_variant.  The first four are the pages'

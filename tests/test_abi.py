@@ -28,7 +28,7 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = set(_declared_functions())
     for n in ("sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_run_variant",
-              "sgemm_run_ex", "sgemm_run_strided_batched", "sgemm_mfma_probe", "sgemm_status_string", "sgemm_variant_name"):
+              "sgemm_run_ex", "sgemm_run_strided_batched", "vector_add", "sgemm_mfma_probe", "sgemm_status_string", "sgemm_variant_name"):
         assert n in names
 
 
@@ -97,6 +97,9 @@ def test_destroy_without_create():
     ((0, 0, 4, 4, 4, 4, 4, 4, 0, 0, 0, 1), "SGEMM_ERR_NOT_INITIALIZED"),  # one product
     ((0, 0, 4, 4, 4, 4, 4, 4, 0, 0, 16, -1), "SGEMM_ERR_INVALID_VALUE"),  # negative batch
     ((0, 0, 4, 4, 4, 4, 4, 4, 0, 0, 16, 2 ** 31), "SGEMM_ERR_TOO_LARGE"),
+    # one 256-thread work-group per product: 2^24 of them is 2^32 work-items
+    ((0, 0, 64, 64, 4, 4, 64, 64, 0, 0, 4096, 2 ** 24 - 1), "SGEMM_ERR_NOT_INITIALIZED"),
+    ((0, 0, 64, 64, 4, 4, 64, 64, 0, 0, 4096, 2 ** 24), "SGEMM_ERR_TOO_LARGE"),
 ])
 def test_general_host_side_argument_checks(args, status):
     lib = sg.load_library()
@@ -118,3 +121,17 @@ def test_general_null_operands():
     assert sg.sgemm_status_string(rc) == "SGEMM_ERR_INVALID_VALUE"
     rc = lib.sgemm_run_ex(0, 0, 4, 4, 4, 1.0, 1, 4, 1, 4, 1.0, None, 4, None)
     assert sg.sgemm_status_string(rc) == "SGEMM_ERR_INVALID_VALUE"
+
+
+@pytest.mark.parametrize("n,ptr,status", [
+    (-1, 1, "SGEMM_ERR_INVALID_VALUE"),
+    (4, 0, "SGEMM_ERR_INVALID_VALUE"),
+    (2 ** 33 + 1, 1, "SGEMM_ERR_TOO_LARGE"),
+    (2 ** 33, 1, "SGEMM_ERR_NOT_INITIALIZED"),
+    (4, 1, "SGEMM_ERR_NOT_INITIALIZED"),
+    (0, 0, "SGEMM_ERR_NOT_INITIALIZED"),
+])
+def test_vector_add_host_side_argument_checks(n, ptr, status):
+    lib = sg.load_library()
+    rc = lib.vector_add(n, 1, ptr or None, 1, None)
+    assert sg.sgemm_status_string(rc) == status
