@@ -22,6 +22,8 @@ What is here:
 * ``exact_products`` -- exact rational sums for tiny inputs (brute force).
 * ``vector_add`` -- C[i] = A[i] + B[i] correctly rounded to float (the
   blog's experiment 1, "向量加法"), from ``oracle_vector_add`` in oracle.c.
+* ``split_bf16x3`` -- the three bfloat16 pieces x0 + x1 + x2 = x, each the
+  nearest 8-significant-bit value to what is left (``oracle_split_bf16x3``).
 
 Matrices are passed as numpy float32 arrays of shape (rows, ld); the logical
 column count is given separately, so columns ld > cols are padding that the
@@ -76,6 +78,8 @@ def _load():
                                         ctypes.c_double, fp, i64, fp, i64, ctypes.c_double,
                                         fp, i64, dp, i64, dp, i64, ctypes.c_int]
     lib.oracle_sgemm_ex_f64.restype = ctypes.c_int
+    lib.oracle_split_bf16x3.argtypes = [i64, fp, fp, fp, fp]
+    lib.oracle_split_bf16x3.restype = ctypes.c_int
     lib.oracle_vector_add.argtypes = [i64, fp, fp, fp]
     lib.oracle_vector_add.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
@@ -272,3 +276,22 @@ def vector_add(A: np.ndarray, B: np.ndarray) -> np.ndarray:
     if rc != 0:
         raise ValueError(f"oracle_vector_add rejected its arguments (rc={rc})")
     return C
+
+
+def split_bf16x3(x: np.ndarray):
+    """Return (p0, p1, p2): uint16 bfloat16 bit patterns, same shape as x
+    (float32), with x = p0 + p1 + p2 exactly for 2^-100 <= |x| <= 3.38e38."""
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.float32:
+        raise TypeError("x must be float32")
+    flat = x.reshape(-1)
+    out = [np.empty(flat.shape, dtype=np.uint16) for _ in range(3)]
+    rc = _load().oracle_split_bf16x3(flat.shape[0], _ptr(flat), *(_ptr(o) for o in out))
+    if rc != 0:
+        raise ValueError(f"oracle_split_bf16x3 rejected its arguments (rc={rc})")
+    return tuple(o.reshape(x.shape) for o in out)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """float32 values of bfloat16 bit patterns (the patterns are the high half)."""
+    return (np.asarray(bits, dtype=np.uint32) << np.uint32(16)).view(np.float32)

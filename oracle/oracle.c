@@ -30,6 +30,7 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <math.h>
+#include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -193,6 +194,57 @@ int oracle_vector_add(int64_t n, const float *A, const float *B, float *C)
         return ORACLE_BAD_ARG;
     for (int64_t i = 0; i < n; ++i)
         C[i] = (float)((double)A[i] + (double)B[i]);
+    return ORACLE_OK;
+}
+
+/*
+ * Three-way split of a float into bfloat16 pieces, x = x0 + x1 + x2.  The
+ * article "硬件加速原理：CUDA核函数优化矩阵乘法的内存访问模式" names tensor
+ * (matrix) cores as the next step (its closing summary, and the note under
+ * its performance table) but gives no method; the reading taken here is the
+ * usual one for carrying single precision through low-precision matrix
+ * cores: split each operand into pieces the cores take exactly.  bfloat16
+ * keeps the float exponent and 8 significant bits.  Each piece is the value with 8 significant bits nearest
+ * to what is left, ties to even:
+ *   x0 = rn8(x),  x1 = rn8(x - x0),  x2 = rn8(x - x0 - x1).
+ * rn8 is written from its definition: x = f * 2^e with 1/2 <= |f| < 1, and
+ * the result is nearbyint(f * 2^8) * 2^(e - 8) (nearbyint rounds to nearest
+ * even in the default rounding mode).  For 2^-100 <= |x| <= 3.38e38 the
+ * three pieces are normal bfloat16 values and their sum is x exactly; that is
+ * the range the split is specified for.  Outputs are the bfloat16 bit
+ * patterns (the high 16 bits of each piece as a float).  Returns
+ * ORACLE_BAD_ARG for n < 0 or a null pointer with n > 0.
+ */
+static double rn8(double x)
+{
+    if (x == 0.0 || !isfinite(x))
+        return x;
+    int e;
+    const double f = frexp(x, &e);
+    return ldexp(nearbyint(ldexp(f, 8)), e - 8);
+}
+
+static uint16_t bf16_bits(double v)
+{
+    const float f = (float)v;  /* exact: v has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+int oracle_split_bf16x3(int64_t n, const float *x, uint16_t *p0, uint16_t *p1, uint16_t *p2)
+{
+    if (n < 0 || (n > 0 && (!x || !p0 || !p1 || !p2)))
+        return ORACLE_BAD_ARG;
+    for (int64_t i = 0; i < n; ++i) {
+        const double v = (double)x[i];
+        const double x0 = rn8(v);
+        const double x1 = rn8(v - x0);      /* v - x0 is exact in double */
+        const double x2 = rn8(v - x0 - x1);
+        p0[i] = bf16_bits(x0);
+        p1[i] = bf16_bits(x1);
+        p2[i] = bf16_bits(x2);
+    }
     return ORACLE_OK;
 }
 

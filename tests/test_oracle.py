@@ -432,3 +432,86 @@ def test_vector_add_special_values():
     assert oracle.vector_add(np.zeros(0, np.float32), np.zeros(0, np.float32)).shape == (0,)
     with pytest.raises(ValueError):
         oracle.vector_add(np.zeros(3, np.float32), np.zeros(4, np.float32))
+
+
+# ---------------------------------------------------------------- bf16 split
+# Pins of oracle.split_bf16x3: exactness of x0 + x1 + x2 = x, each piece the
+# nearest bfloat16 to what is left (checked against the adjacent bfloat16
+# values, whose bit patterns differ by one), and the products kept.
+
+def _wide_floats(n, seed, lo=-90, hi=120):
+    g = np.random.default_rng(seed)
+    m = g.uniform(1.0, 2.0, n) * np.where(g.random(n) < 0.5, -1.0, 1.0)
+    return (m * np.exp2(g.integers(lo, hi, n))).astype(np.float32)
+
+
+def _nearest_bf16_ok(target: Fraction, bits: int) -> bool:
+    """bits (a bfloat16 pattern) is a nearest bfloat16 to target, ties to even."""
+    val = Fraction(float(oracle.bf16_to_f32(np.uint16(bits))))
+    d = abs(val - target)
+    mag, sign = bits & 0x7FFF, bits & 0x8000
+    for nb_mag in (mag - 1, mag + 1):
+        if nb_mag < 0 or nb_mag >= 0x7F80:
+            continue
+        nb = Fraction(float(oracle.bf16_to_f32(np.uint16(sign | nb_mag))))
+        dn = abs(nb - target)
+        if dn < d or (dn == d and (bits & 1)):
+            return False
+    if mag == 0:  # zero: the smallest normals on either side must not be closer
+        for nb_bits in (0x0080, 0x8080):
+            if abs(Fraction(float(oracle.bf16_to_f32(np.uint16(nb_bits)))) - target) < d:
+                return False
+    return True
+
+
+def test_split_is_exact_and_pieces_are_bf16():
+    x = _wide_floats(200_000, 5)
+    p = oracle.split_bf16x3(x)
+    v = [oracle.bf16_to_f32(q).astype(np.float64) for q in p]
+    assert np.array_equal(v[0] + v[1] + v[2], x.astype(np.float64))  # exact in double
+    assert np.all(np.abs(v[1]) <= np.abs(x) * 2.0 ** -8)
+    assert np.all(np.abs(v[2]) <= np.abs(x) * 2.0 ** -16)
+
+
+def test_split_pieces_are_nearest_brute_force():
+    x = np.concatenate([_wide_floats(1500, 6),
+                        np.float32([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 0.0, 2.0,
+                                    1 - 2 ** -9, 3.14159265])])
+    p0, p1, p2 = oracle.split_bf16x3(x)
+    for i in range(x.shape[0]):
+        left = Fraction(float(x[i]))
+        for q in (p0[i], p1[i], p2[i]):
+            assert _nearest_bf16_ok(left, int(q)), (x[i], hex(int(q)))
+            left -= Fraction(float(oracle.bf16_to_f32(q)))
+        assert left == 0
+
+
+def test_split_worked_ties():
+    x = np.float32([1 + 2 ** -8, 1 + 3 * 2 ** -8, -0.0])
+    v = [oracle.bf16_to_f32(q) for q in oracle.split_bf16x3(x)]
+    assert (v[0][0], v[1][0], v[2][0]) == (1.0, 2.0 ** -8, 0.0)          # tie to even: down
+    assert (v[0][1], v[1][1], v[2][1]) == (1 + 2 ** -6, -(2.0 ** -8), 0.0)  # tie to even: up
+    assert v[0][2] == 0.0 and np.signbit(v[0][2])
+
+
+def test_split_nearest_check_catches_truncation():
+    """A planted truncating split (high half of the float bits) is not nearest."""
+    x = _wide_floats(64, 7)
+    trunc = (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    bad = [i for i in range(64) if not _nearest_bf16_ok(Fraction(float(x[i])), int(trunc[i]))]
+    assert len(bad) > 10
+
+
+def test_six_of_nine_products_meet_the_single_precision_bound():
+    """Keeping the products x_i y_j with i + j <= 2 leaves an error below
+    2^-22 |x y|; keeping only i + j <= 1 (three products) exceeds the
+    1e-5 relative tolerance on some pairs, which is why six are kept."""
+    x = _wide_floats(20_000, 8, -20, 20)
+    y = _wide_floats(20_000, 9, -20, 20)
+    px = [oracle.bf16_to_f32(q).astype(np.float64) for q in oracle.split_bf16x3(x)]
+    py = [oracle.bf16_to_f32(q).astype(np.float64) for q in oracle.split_bf16x3(y)]
+    exact = x.astype(np.float64) * y.astype(np.float64)
+    six = sum(px[i] * py[j] for i in range(3) for j in range(3) if i + j <= 2)
+    three = sum(px[i] * py[j] for i in range(3) for j in range(3) if i + j <= 1)
+    assert np.max(np.abs(six - exact) / np.abs(exact)) < 2.0 ** -22
+    assert np.max(np.abs(three - exact) / np.abs(exact)) > 1e-5
