@@ -265,6 +265,65 @@ def general_table(settle: float) -> list[dict]:
 
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bfloat16 matrix peak, published
+
+
+def bf16x3_table(steps: int, warmup: int, settle: float) -> list[dict]:
+    """Time sgemm_run_bf16x3 (split + product, one call) on the square
+    workloads and report single-precision-equivalent TFLOP/s (2 M N K per
+    call) next to the bfloat16 matrix-core rate of its six piece products
+    (6 * 2 M N K per call, whole call)."""
+    import torch
+
+    import dense_fp32_matrix_03_amd as sg
+    from dense_fp32_matrix_03_amd import inputs
+
+    rows = []
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    for name in ("sgemm_1024x1024x1024_uniform_seed1", SECONDARY, HEADLINE):
+        w = inputs.BY_NAME[name]
+        A, B = inputs.make_inputs(w)
+        dA = torch.from_numpy(A).cuda()
+        dB = torch.from_numpy(B).cuda()
+        del A, B
+        dC = torch.empty((w.M, w.ldc), dtype=torch.float32, device="cuda")
+        nbytes = sg.sgemm_bf16x3_workspace_size(w.M, w.N, w.K)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+        def step():
+            sg.sgemm_run_bf16x3(w.M, w.N, w.K, dA, w.lda, dB, w.ldb, dC, w.ldc, ws, nbytes, h)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t_end = time.perf_counter() + settle
+        while time.perf_counter() < t_end:
+            for _ in range(10):
+                step()
+            torch.cuda.synchronize()
+        n = steps if w.flops > 1e12 else max(steps, 100)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(n):
+            step()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / n
+        tf = w.flops / (ms * 1e-3) / 1e12
+        r = {"kernel": "bf16x3", "workload": w.name, "steps": n, "ms": round(ms, 5),
+             "tflops_fp32_equivalent": round(tf, 2),
+             "pct_of_fp32_peak": round(100 * tf / PEAK_TFLOPS, 1),
+             "bf16_tflops": round(6 * tf, 1),
+             "pct_of_bf16_peak": round(100 * 6 * tf / BF16_PEAK_TFLOPS, 1),
+             "workspace_bytes": nbytes,
+             "output_finite": bool(torch.isfinite(dC[:, :w.N]).all().item())}
+        print(json.dumps(r), flush=True)
+        rows.append(r)
+        del dA, dB, dC, ws
+        torch.cuda.empty_cache()
+    return rows
 
 
 def vector_add_table(steps: int, settle: float) -> list[dict]:
@@ -350,6 +409,9 @@ def main(argv=None) -> int:
     ap.add_argument("--vector-add", action="store_true",
                     help="time vector_add (n = 2^24 with resident and rotating arrays, "
                          "n = 2^28) and print its effective bandwidth, one JSON line each")
+    ap.add_argument("--bf16x3", action="store_true",
+                    help="time sgemm_run_bf16x3 (single precision on the bfloat16 matrix "
+                         "cores) at 1024^3, 2048^3 and 8192^3, one JSON line each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -384,6 +446,10 @@ def main(argv=None) -> int:
     variant = sg.VARIANTS[a.variant] if a.variant in sg.VARIANTS else int(a.variant)
     if a.table:
         workload_table(variant)
+        sg.sgemm_destroy()
+        return 0
+    if a.bf16x3:
+        bf16x3_table(a.steps, a.warmup, a.settle)
         sg.sgemm_destroy()
         return 0
     if a.vector_add:

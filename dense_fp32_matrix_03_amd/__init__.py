@@ -71,6 +71,10 @@ def load_library(path: str = LIB_PATH):
     lib.sgemm_run_strided_batched.argtypes = [ci, ci, i64, i64, i64, f32, vp, i64, i64, vp, i64,
                                               i64, f32, vp, i64, i64, i64, vp]
     lib.sgemm_run_strided_batched.restype = ci
+    lib.sgemm_bf16x3_workspace_size.argtypes = [i64, i64, i64]
+    lib.sgemm_bf16x3_workspace_size.restype = i64
+    lib.sgemm_run_bf16x3.argtypes = gemm_args[:-1] + [vp, i64, vp]
+    lib.sgemm_run_bf16x3.restype = ci
     lib.vector_add.argtypes = [i64, vp, vp, vp, vp]
     lib.vector_add.restype = ci
     lib.sgemm_mfma_probe.argtypes = [ci, vp, vp, vp, vp]
@@ -144,6 +148,22 @@ def sgemm_run_strided_batched(transA, transB, M, N, K, alpha, A, lda, strideA, B
     _check("sgemm_run_strided_batched", load_library().sgemm_run_strided_batched(
         int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda, strideA, _ptr(B), ldb,
         strideB, float(beta), _ptr(C), ldc, strideC, batch, _stream(stream)))
+
+
+def sgemm_bf16x3_workspace_size(M, N, K) -> int:
+    """Workspace bytes sgemm_run_bf16x3 needs (include/sgemm_bf16x3.h)."""
+    r = load_library().sgemm_bf16x3_workspace_size(M, N, K)
+    if r < 0:
+        raise SgemmError("sgemm_bf16x3_workspace_size", int(r))
+    return int(r)
+
+
+def sgemm_run_bf16x3(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
+                     stream=None) -> None:
+    """C = A x B on the bfloat16 matrix cores (three-piece split)."""
+    _check("sgemm_run_bf16x3", load_library().sgemm_run_bf16x3(
+        M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(workspace), workspace_bytes,
+        _stream(stream)))
 
 
 def vector_add(n, A, B, C, stream=None) -> None:

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsgemm.so")
-SOURCES = ["api.hip", "mfma_kernels.hip", "valu_kernels.hip", "vector_add.hip"]
+SOURCES = ["api.hip", "mfma_kernels.hip", "valu_kernels.hip", "vector_add.hip", "bf16x3.hip"]
 ARCH = "gfx950"
 
 

@@ -1,6 +1,6 @@
-// api.hip -- the C interface declared in include/sgemm.h and
-// include/vector_add.h: argument checks, device check, and the choice of
-// kernel configuration for each call.
+// api.hip -- the C interface declared in include/sgemm.h,
+// include/sgemm_bf16x3.h and include/vector_add.h: argument checks, device
+// check, and the choice of kernel configuration for each call.
 #include <stdint.h>
 
 #include <atomic>
@@ -9,6 +9,7 @@
 
 #include "dispatch.hpp"
 #include "sgemm.h"
+#include "sgemm_bf16x3.h"
 #include "vector_add.h"
 
 namespace {
@@ -51,6 +52,11 @@ int current_device_info(DeviceInfo *out) {
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 // A launch's work-items (work-groups x threads) must fit 32 bits.
 constexpr int64_t kMaxWorkItems = (int64_t(1) << 32) - 1;
+// bfloat16-split product: K up to 2^21 keeps a 256-row slice of a plane
+// within a buffer descriptor's range; (M + N) * Kp up to 2^34 keeps the split
+// launches below 2^32 work-items.
+constexpr int64_t kMaxBf16x3K = int64_t(1) << 21;
+constexpr int64_t kMaxBf16x3Split = int64_t(1) << 34;
 
 // Whether `batch` products of M x N, one `threads`-wide work-group per
 // tile x tile block of C, fit one launch.  The matrix-core kernels use at
@@ -235,14 +241,76 @@ int sgemm_run_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float 
                                    ldc, 0, 1, stream);
 }
 
+int64_t sgemm_bf16x3_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_INVALID_VALUE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxBf16x3K) return SGEMM_ERR_TOO_LARGE;
+  const int64_t Kp = (K + 31) / 32 * 32;
+  if ((M + N) * Kp > kMaxBf16x3Split) return SGEMM_ERR_TOO_LARGE;
+  return 6 * Kp * (M + N);  // three 2-byte planes of each operand
+}
+
+int sgemm_run_bf16x3(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                     const float *B, int64_t ldb, float *C, int64_t ldc, void *workspace,
+                     int64_t workspace_bytes, void *stream) {
+  int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc);
+  if (rc != SGEMM_OK) return rc;
+  const int64_t need = sgemm_bf16x3_workspace_size(M, N, K);
+  if (need < 0) return (int)need;
+  if (M > 0 && N > 0 && K > 0 &&
+      (!workspace || !aligned16(workspace) || workspace_bytes < need))
+    return SGEMM_ERR_INVALID_VALUE;
+  if (!g_ready.load(std::memory_order_acquire)) return SGEMM_ERR_NOT_INITIALIZED;
+  if (M == 0 || N == 0) return SGEMM_OK;
+  DeviceInfo di;
+  rc = current_device_info(&di);
+  if (rc != SGEMM_OK) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  hipError_t err;
+  if (K == 0) {
+    sgemm::GemmArgs z;
+    z.M = (int)M;
+    z.N = (int)N;
+    z.K = 0;
+    z.A = A;
+    z.lda = lda;
+    z.B = B;
+    z.ldb = ldb;
+    z.C = C;
+    z.ldc = ldc;
+    err = sgemm::launch_scale(z, s);  // the empty sum
+  } else {
+    const int64_t Kp = (K + 31) / 32 * 32;
+    unsigned short *wa = static_cast<unsigned short *>(workspace);
+    unsigned short *wb = wa + 3 * M * Kp;
+    err = sgemm::launch_split(A, lda, B, ldb, (int)M, (int)N, (int)K, (int)Kp, wa, wb, s);
+    if (err == hipSuccess) {
+      sgemm::Bf16x3Args p;
+      p.M = (int)M;
+      p.N = (int)N;
+      p.Kp = Kp;
+      p.a = wa;
+      p.b = wb;
+      p.plane_a = M * Kp;
+      p.plane_b = N * Kp;
+      p.C = C;
+      p.ldc = ldc;
+      err = sgemm::launch_bf16x3_gemm(sgemm::choose_mfma_tile(M, N, di.cus), p, s);
+      if (err == hipErrorInvalidValue) return SGEMM_ERR_TOO_LARGE;
+    }
+  }
+  return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
 int sgemm_mfma_probe(int which, const float *A, const float *B, float *C, void *stream) {
-  if ((which != 0 && which != 1) || !A || !B || !C) return SGEMM_ERR_INVALID_VALUE;
+  if (which < 0 || which > 2 || !A || !B || !C) return SGEMM_ERR_INVALID_VALUE;
   if (!g_ready.load(std::memory_order_acquire)) return SGEMM_ERR_NOT_INITIALIZED;
   DeviceInfo di;
   const int rc = current_device_info(&di);
   if (rc != SGEMM_OK) return rc;
-  const hipError_t err =
-      sgemm::launch_mfma_probe(which, A, B, C, reinterpret_cast<hipStream_t>(stream));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t err = which == 2 ? sgemm::launch_bf16_probe(A, B, C, s)
+                                    : sgemm::launch_mfma_probe(which, A, B, C, s);
   return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 

@@ -1,0 +1,518 @@
+// bf16x3.hip -- the single-precision product C = A x B carried through the
+// bfloat16 matrix cores of gfx950.
+//
+// The article "硬件加速原理：CUDA核函数优化矩阵乘法的内存访问模式" names tensor
+// (matrix) cores as the next step beyond its FP32 kernels.  On gfx950 the
+// bfloat16 matrix instruction has 16 times the throughput of the FP32 one,
+// but a bfloat16 keeps only 8 significant bits.  So each operand value is
+// split into three bfloat16 pieces that sum to it exactly,
+//   x = x0 + x1 + x2,  x0 = rn(x), x1 = rn(x - x0), x2 = x - x0 - x1
+// (rn: nearest bfloat16, ties to even; |x1| <= 2^-8 |x|, |x2| <= 2^-16 |x|),
+// and the product keeps the six piece products whose order adds up to at
+// most 2:  a0 b0 + a0 b1 + a1 b0 + a0 b2 + a1 b1 + a2 b0.  The three dropped
+// products are below 2^-23 |a b| together, under single-precision rounding;
+// each piece product is exact in the FP32 accumulator.  Six bfloat16
+// instructions cost 6/16 of one FP32 instruction.
+//
+// Two passes:
+//  1. split: each operand is read once from HBM and written to the caller's
+//     workspace as three bfloat16 planes with k contiguous, K padded with
+//     zeros to Kp (a multiple of 32): A as [3][M][Kp], B transposed as
+//     [3][N][Kp].  Memory-bound, like the vector add.
+//  2. product: the buffer-to-LDS pipeline of the FP32 kernel (mfma_dma.hpp)
+//     over the six planes, v_mfma_f32_32x32x16_bf16 on 32 x 32 blocks.
+#include "common.hpp"
+#include "dispatch.hpp"
+#include "mfma_dma.hpp"
+
+namespace sgemm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_32x32x16_bf16: D(32x32) = A(32x16) B(16x32) + C, one wave.
+// Lane l supplies the 8 values A(l % 32, 8*(l/32) + e) and B(8*(l/32) + e,
+// l % 32), e < 8; the accumulator layout is that of the FP32 32x32
+// instruction (acc32_row).
+__device__ __forceinline__ f32x16 mfma32x32x16_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// bfloat16 bit pattern of the float nearest to x with 8 significant bits,
+// ties to even (x finite): adding 0x7fff plus the lowest kept bit to the
+// float's bits carries into the kept half exactly when the dropped half is
+// above one half, or one half with an odd kept half.
+__device__ __forceinline__ unsigned rne_bf16_bits(float x) {
+  const unsigned u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_value(unsigned h) { return __uint_as_float(h << 16); }
+
+// Split 8 floats into three 16-byte chunks of bfloat16 (element e in the
+// low half of word e/2 for even e).
+__device__ __forceinline__ void split8(const float v[8], u32x4 out[3]) {
+  unsigned h[3][8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const unsigned h0 = rne_bf16_bits(v[e]);
+    const float r1 = v[e] - bf16_bits_value(h0);  // exact
+    const unsigned h1 = rne_bf16_bits(r1);
+    const float r2 = r1 - bf16_bits_value(h1);    // exact, at most 8 significant bits
+    h[0][e] = h0;
+    h[1][e] = h1;
+    h[2][e] = rne_bf16_bits(r2);
+  }
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) out[p][w] = (h[p][2 * w] & 0xffffu) | (h[p][2 * w + 1] << 16);
+}
+
+// ------------------------------------------------------------------ split
+// One launch splits both operands: work-groups [0, blocks_a) take A, the
+// rest take B.
+//
+// A (k along its columns, M x K, leading dimension lda): one thread per 8
+// consecutive k of one row, k >= K read as 0.  VA: 16-byte aligned base and
+// lda % 4 == 0, so the 8 values come in two 16-byte loads where they lie
+// inside the row.
+//
+// B (k along its rows, K x N, leading dimension ldb), written transposed as
+// [N][Kp]: a 64 (k) x 64 (n) tile goes through LDS (rows read as 16 float4
+// per k row where VB: 16-byte aligned, ldb % 4 == 0, N % 4 == 0); then lane l
+// of each group of 8 takes k-chunk l % 8 of one column, so 8 lanes write 128
+// contiguous bytes of a plane row.
+constexpr int kSplitT = 64;
+
+struct SplitArgs {
+  const float *A;
+  long lda;
+  const float *B;
+  long ldb;
+  int M, N, K, Kp;
+  u32x4 *wa, *wb;  // plane 0 of A's and of B's planes (16-byte chunks)
+  long blocks_a;
+  int tiles_n;
+};
+
+template <bool VA, bool VB>
+__global__ void __launch_bounds__(256) split_kernel(SplitArgs p) {
+  __shared__ float tile[kSplitT][kSplitT + 1];
+  const int tid = threadIdx.x;
+  const int cpr = p.Kp / 8;
+  if ((long)blockIdx.x < p.blocks_a) {
+    const long plane = (long)p.M * cpr;
+    const long q = (long)blockIdx.x * 256 + tid;
+    if (q >= plane) return;
+    const int row = (int)(q / cpr), c = (int)(q % cpr);
+    const int k0 = c * 8;
+    const float *x = p.A + (long)row * p.lda + k0;
+    float v[8];
+    if (VA && k0 + 8 <= p.K) {
+      const f32x4 lo = *reinterpret_cast<const f32x4 *>(x);
+      const f32x4 hi = *reinterpret_cast<const f32x4 *>(x + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = lo[e];
+        v[4 + e] = hi[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = k0 + e < p.K ? x[e] : 0.f;
+    }
+    u32x4 out[3];
+    split8(v, out);
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) p.wa[pl * plane + q] = out[pl];
+    return;
+  }
+  const long b = (long)blockIdx.x - p.blocks_a;
+  const int tn = (int)(b % p.tiles_n), tk = (int)(b / p.tiles_n);
+  const int n0 = tn * kSplitT, k0 = tk * kSplitT;
+  if constexpr (VB) {
+    // 64 rows x 16 float4: 4 per thread.
+#pragma unroll
+    for (int i = 0; i < kSplitT * kSplitT / 4 / 256; ++i) {
+      const int f = tid + i * 256;
+      const int r = f / (kSplitT / 4), c4 = (f % (kSplitT / 4)) * 4;
+      const int k = k0 + r, n = n0 + c4;
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+      if (k < p.K && n < p.N) t = *reinterpret_cast<const f32x4 *>(p.B + (long)k * p.ldb + n);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[r][c4 + e] = t[e];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kSplitT * kSplitT / 256; ++i) {
+      const int r = tid / kSplitT + i * (256 / kSplitT), c = tid % kSplitT;
+      const int k = k0 + r, n = n0 + c;
+      tile[r][c] = (k < p.K && n < p.N) ? p.B[(long)k * p.ldb + n] : 0.f;
+    }
+  }
+  __syncthreads();
+  const long plane = (long)p.N * cpr;
+#pragma unroll
+  for (int i = 0; i < kSplitT * (kSplitT / 8) / 256; ++i) {
+    const int task = tid + i * 256;
+    const int kc = task % 8, c = task / 8;
+    const int n = n0 + c, kchunk = k0 / 8 + kc;
+    if (n >= p.N || kchunk >= cpr) continue;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[kc * 8 + e][c];
+    u32x4 out[3];
+    split8(v, out);
+    const long q = (long)n * cpr + kchunk;
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) p.wb[pl * plane + q] = out[pl];
+  }
+}
+
+hipError_t launch_split(const float *A, long lda, const float *B, long ldb, int M, int N, int K,
+                        int Kp, void *wa, void *wb, hipStream_t stream) {
+  SplitArgs p;
+  p.A = A;
+  p.lda = lda;
+  p.B = B;
+  p.ldb = ldb;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.Kp = Kp;
+  p.wa = reinterpret_cast<u32x4 *>(wa);
+  p.wb = reinterpret_cast<u32x4 *>(wb);
+  p.blocks_a = ((long)M * (Kp / 8) + 255) / 256;
+  p.tiles_n = (N + kSplitT - 1) / kSplitT;
+  const long blocks_b = (long)p.tiles_n * ((Kp + kSplitT - 1) / kSplitT);
+  const dim3 grid((unsigned)(p.blocks_a + blocks_b)), block(256);
+  const bool va = (reinterpret_cast<uintptr_t>(A) & 15u) == 0 && lda % 4 == 0;
+  const bool vb = (reinterpret_cast<uintptr_t>(B) & 15u) == 0 && ldb % 4 == 0 && N % 4 == 0;
+  if (va && vb)
+    hipLaunchKernelGGL((split_kernel<true, true>), grid, block, 0, stream, p);
+  else if (va)
+    hipLaunchKernelGGL((split_kernel<true, false>), grid, block, 0, stream, p);
+  else if (vb)
+    hipLaunchKernelGGL((split_kernel<false, true>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((split_kernel<false, false>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- product
+// Chunk swizzle of the bfloat16 slice images: row `row` of BK values has
+// BK/8 16-byte chunks; chunk c is stored at c ^ swz(row).  With 32-byte rows
+// (BK = 16) swz = bit 2 ^ bit 3 of the row, with 64-byte rows (BK = 32) the
+// FP32 kernel's 4-chunk swizzle: either way the 128-bit operand reads of 8
+// and of 16 consecutive rows fall on disjoint banks.
+template <int BK>
+__device__ __forceinline__ int bf16_swizzle(int row) {
+  static_assert(BK == 16 || BK == 32, "16 or 32 bfloat16 per slice row");
+  if constexpr (BK == 16)
+    return ((row >> 2) ^ (row >> 3)) & 1;
+  else
+    return kc_swizzle<16, true>(row);
+}
+
+// Barrier that first retires all but this wave's N most recent
+// buffer-to-LDS loads: s_waitcnt vmcnt(N) (vmcnt is 6 bits, split over bits
+// 3:0 and 15:14 of SIMM16; expcnt and lgkmcnt at their "don't wait" maxima),
+// then the work-group barrier.
+template <int N>
+__device__ __forceinline__ void dma_barrier_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xf << 8) | ((N >> 4) << 14));
+  __syncthreads();
+}
+
+// NS LDS stages: slice t lives in stage t % NS; the loads of slice t + NS
+// go out right after the barrier that ends slice t, so each load has NS - 1
+// slices of time to arrive.
+//
+// Software pipeline (MODE):
+//   0  per k step: read the three planes' fragments, then the six products;
+//   1  the next k step's fragments are read before this step's products are
+//      issued (two full fragment sets live);
+//   2  plane by plane: plane 1 is read while the plane-0 product runs, plane
+//      2 while the two products of order 1 run, and the next k step's plane
+//      0 while the three of order 2 run (four plane sets live).
+template <int BM, int BN, int BK, int WM, int WN, int MODE, int NS>
+__global__ void __launch_bounds__(WM *WN *kWave)
+bf16x3_gemm_kernel(Bf16x3Args p, int tiles_m, int tiles_n, int group_m) {
+  static_assert(NS >= 2 && NS <= 4, "two to four stages");
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int CPR = BK / 8;              // 16-byte chunks per image row
+  constexpr int KS = BK / 16;              // matrix-core k steps per slice
+  constexpr int NBA = BM * BK * 2 / 1024;  // 1 KiB loads per plane of A
+  constexpr int NBB = BN * BK * 2 / 1024;
+  static_assert(NBA % NW == 0 && NBB % NW == 0, "loads must split evenly over the waves");
+  constexpr int QA = NBA / NW, QB = NBB / NW;  // loads per wave per plane
+  constexpr int PA = BM * BK, PB = BN * BK;    // bfloat16 per plane image
+
+  constexpr int LPS = 3 * (QA + QB);           // loads per wave per slice
+  static_assert(LPS * (NS - 1) < 64, "outstanding loads must fit vmcnt");
+
+  __shared__ __attribute__((aligned(1024))) unsigned short As0[3 * PA];
+  __shared__ __attribute__((aligned(1024))) unsigned short As1[3 * PA];
+  __shared__ __attribute__((aligned(1024))) unsigned short As2[NS > 2 ? 3 * PA : 8];
+  __shared__ __attribute__((aligned(1024))) unsigned short As3[NS > 3 ? 3 * PA : 8];
+  __shared__ __attribute__((aligned(1024))) unsigned short Bs0[3 * PB];
+  __shared__ __attribute__((aligned(1024))) unsigned short Bs1[3 * PB];
+  __shared__ __attribute__((aligned(1024))) unsigned short Bs2[NS > 2 ? 3 * PB : 8];
+  __shared__ __attribute__((aligned(1024))) unsigned short Bs3[NS > 3 ? 3 * PB : 8];
+  auto stage_a = [&](auto S) -> unsigned short * {
+    constexpr int st = decltype(S)::value;
+    if constexpr (st == 0) return As0;
+    else if constexpr (st == 1) return As1;
+    else if constexpr (st == 2) return As2;
+    else return As3;
+  };
+  auto stage_b = [&](auto S) -> unsigned short * {
+    constexpr int st = decltype(S)::value;
+    if constexpr (st == 0) return Bs0;
+    else if constexpr (st == 1) return Bs1;
+    else if constexpr (st == 2) return Bs2;
+    else return Bs3;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave / WN, wn = wave % WN;
+  const int r32 = lane % 32, half = lane / 32;
+
+  const int id = xcd_contiguous_id(blockIdx.x, gridDim.x);
+  int tm, tn;
+  grouped_tile(id, tiles_m, tiles_n, group_m, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const long Kp = p.Kp;
+
+  // Lane offsets (bytes from the slice origin of a plane), shared by the
+  // three planes; rows past M (N) read as zeros.
+  unsigned offA[QA], offB[QB];
+#pragma unroll
+  for (int q = 0; q < QA; ++q) {
+    const int f = (wave + q * NW) * kWave + lane;
+    const int row = f / CPR, c = (f % CPR) ^ bf16_swizzle<BK>(row);
+    offA[q] = m0 + row < p.M ? (unsigned)((row * Kp + c * 8) * 2) : kOutOfRange;
+  }
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    const int f = (wave + q * NW) * kWave + lane;
+    const int row = f / CPR, c = (f % CPR) ^ bf16_swizzle<BK>(row);
+    offB[q] = n0 + row < p.N ? (unsigned)((row * Kp + c * 8) * 2) : kOutOfRange;
+  }
+
+  const int nk = (int)(Kp / BK);
+  auto dma = [&](auto S, int t) {
+    unsigned short *as = stage_a(S);
+    unsigned short *bs = stage_b(S);
+    const long k0 = t < nk ? (long)t * BK : 0;
+    const int records = t < nk ? kBufferRecords : 0;
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) {
+      const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<unsigned short *>(p.a + pl * p.plane_a + (long)m0 * Kp + k0), 0, records,
+          kRawBufferWord3);
+      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<unsigned short *>(p.b + pl * p.plane_b + (long)n0 * Kp + k0), 0, records,
+          kRawBufferWord3);
+#pragma unroll
+      for (int q = 0; q < QA; ++q)
+        lds_dma<true>(ra, reinterpret_cast<float *>(as + pl * PA + (wave + q * NW) * 512), offA[q]);
+#pragma unroll
+      for (int q = 0; q < QB; ++q)
+        lds_dma<true>(rb, reinterpret_cast<float *>(bs + pl * PB + (wave + q * NW) * 512), offB[q]);
+    }
+  };
+
+  // Fragments of one plane for k step j: lane reads row (wave row base +
+  // i*32 + r32), logical chunk 2j + half.  The row's swizzle depends only on
+  // r32 (row mod 16).
+  const int sw = bf16_swizzle<BK>(r32);
+  struct Plane {
+    bf16x8 a[FM];
+    bf16x8 b[FN];
+  };
+  auto read = [&](auto S, int j, int pl, Plane &d) {
+    const unsigned short *as = stage_a(S) + pl * PA;
+    const unsigned short *bs = stage_b(S) + pl * PB;
+    const int ch = ((2 * j + half) ^ sw) * 8;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      d.a[i] = *reinterpret_cast<const bf16x8 *>(as + (wm * WTM + i * 32 + r32) * BK + ch);
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+      d.b[i] = *reinterpret_cast<const bf16x8 *>(bs + (wn * WTN + i * 32 + r32) * BK + ch);
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // acc += (a pieces of x) (b pieces of y)
+  auto mma = [&](const Plane &x, const Plane &y) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16_bf16(x.a[i], y.b[j], acc[i][j]);
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  Plane c0, c1, c2, n0p, n1p, n2p;
+
+  // Slice t is in stage S = t % NS; slice t + 1 is in (or on its way to) SN.
+  // The barrier that ends the slice waits until slice t + 1 has landed (the
+  // loads of the NS - 2 slices after it may stay in flight).
+  auto end_barrier = [&]() { dma_barrier_keep<LPS * (NS - 2)>(); };
+  auto slice = [&](auto S, int t) {
+    constexpr int s = decltype(S)::value;
+    using SN = std::integral_constant<int, (s + 1) % NS>;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      const bool last = j + 1 == KS;
+      if constexpr (MODE == 0) {
+        read(S, j, 0, c0);
+        read(S, j, 1, c1);
+        read(S, j, 2, c2);
+        if (last) {
+          end_barrier();
+          dma(S, t + NS);
+        }
+        mma(c0, c0);
+        mma(c0, c1);
+        mma(c1, c0);
+        mma(c0, c2);
+        mma(c1, c1);
+        mma(c2, c0);
+      } else if constexpr (MODE == 1) {
+        if (!last) {
+          read(S, j + 1, 0, n0p);
+          read(S, j + 1, 1, n1p);
+          read(S, j + 1, 2, n2p);
+        } else {
+          end_barrier();
+          dma(S, t + NS);
+          read(SN(), 0, 0, n0p);  // harmless if there is no slice t+1
+          read(SN(), 0, 1, n1p);
+          read(SN(), 0, 2, n2p);
+        }
+        mma(c0, c0);
+        mma(c0, c1);
+        mma(c1, c0);
+        mma(c0, c2);
+        mma(c1, c1);
+        mma(c2, c0);
+        c0 = n0p;
+        c1 = n1p;
+        c2 = n2p;
+      } else {
+        read(S, j, 1, c1);
+        mma(c0, c0);
+        read(S, j, 2, c2);
+        mma(c0, c1);
+        mma(c1, c0);
+        if (!last) {
+          read(S, j + 1, 0, n0p);
+        } else {
+          end_barrier();
+          dma(S, t + NS);
+          read(SN(), 0, 0, n0p);  // harmless if there is no slice t+1
+        }
+        mma(c0, c2);
+        mma(c1, c1);
+        mma(c2, c0);
+        c0 = n0p;
+      }
+    }
+  };
+
+  dma(S0(), 0);
+  dma(std::integral_constant<int, 1>(), 1);
+  if constexpr (NS > 2) dma(std::integral_constant<int, 2 % NS>(), 2);
+  if constexpr (NS > 3) dma(std::integral_constant<int, 3 % NS>(), 3);
+  dma_barrier_keep<LPS * (NS - 1)>();  // slice 0 has landed
+  if constexpr (MODE == 1) {
+    read(S0(), 0, 0, c0);
+    read(S0(), 0, 1, c1);
+    read(S0(), 0, 2, c2);
+  } else if constexpr (MODE == 2) {
+    read(S0(), 0, 0, c0);
+  }
+  for (int t = 0; t < nk; t += NS) {
+    slice(S0(), t);
+    if (t + 1 < nk) slice(std::integral_constant<int, 1>(), t + 1);
+    if constexpr (NS > 2)
+      if (t + 2 < nk) slice(std::integral_constant<int, 2 % NS>(), t + 2);
+    if constexpr (NS > 3)
+      if (t + 3 < nk) slice(std::integral_constant<int, 3 % NS>(), t + 3);
+  }
+  // The last slices issued loads past K (zero-filling, no memory traffic);
+  // let them retire before the work-group gives up its LDS.
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+
+  const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN + r32;
+  const bool full = (m0 + BM <= p.M) && (n0 + BN <= p.N);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = row0 + i * 32 + acc32_row(lane, e);
+        const int col = col0 + j * 32;
+        if (full || (row < p.M && col < p.N)) p.C[(long)row * p.ldc + col] = acc[i][j][e];
+      }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int MODE, int NS>
+static hipError_t launch_bf16x3_cfg(const Bf16x3Args &p, hipStream_t stream) {
+  if (!dma_offsets_fit(BM, p.Kp / 2, BN, p.Kp / 2)) return hipErrorInvalidValue;
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  hipLaunchKernelGGL((bf16x3_gemm_kernel<BM, BN, BK, WM, WN, MODE, NS>),
+                     dim3((unsigned)((long)tiles_m * tiles_n)), dim3(WM * WN * kWave), 0, stream,
+                     p, tiles_m, tiles_n, 8);
+  return hipGetLastError();
+}
+
+hipError_t launch_bf16x3_gemm(MfmaTile tile, const Bf16x3Args &p, hipStream_t stream) {
+  switch (tile) {
+    case MfmaTile::T256: return launch_bf16x3_cfg<256, 256, 16, 2, 4, 0, 2>(p, stream);
+    case MfmaTile::T128: return launch_bf16x3_cfg<128, 128, 32, 2, 2, 1, 2>(p, stream);
+    case MfmaTile::T64: return launch_bf16x3_cfg<64, 64, 32, 2, 2, 1, 2>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+// One-instruction probe of v_mfma_f32_32x32x16_bf16: A is 32 x 16 and B is
+// 16 x 32, row-major floats that are exact bfloat16 values (their high
+// halves are taken); C is 32 x 32 row-major.
+__global__ void __launch_bounds__(kWave) bf16_probe_kernel(const float *A, const float *B,
+                                                          float *C) {
+  const int l = threadIdx.x;
+  bf16x8 a, b;
+  unsigned short ha[8], hb[8];
+  for (int e = 0; e < 8; ++e) {
+    ha[e] = (unsigned short)(__float_as_uint(A[(l % 32) * 16 + 8 * (l / 32) + e]) >> 16);
+    hb[e] = (unsigned short)(__float_as_uint(B[(8 * (l / 32) + e) * 32 + l % 32]) >> 16);
+  }
+  __builtin_memcpy(&a, ha, sizeof a);
+  __builtin_memcpy(&b, hb, sizeof b);
+  f32x16 acc;
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  acc = mfma32x32x16_bf16(a, b, acc);
+  for (int e = 0; e < 16; ++e) C[acc32_row(l, e) * 32 + l % 32] = acc[e];
+}
+
+hipError_t launch_bf16_probe(const float *A, const float *B, float *C, hipStream_t stream) {
+  hipLaunchKernelGGL(bf16_probe_kernel, dim3(1), dim3(kWave), 0, stream, A, B, C);
+  return hipGetLastError();
+}
+
+}  // namespace sgemm

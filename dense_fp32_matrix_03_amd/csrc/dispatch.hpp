@@ -44,6 +44,30 @@ hipError_t launch_mfma_probe(int which, const float *A, const float *B, float *C
 // 3 register-tiled with a double-buffered LDS pipeline.
 hipError_t launch_valu(int rung, const GemmArgs &p, bool va, bool vb, hipStream_t stream);
 
+// ---- single precision through the bfloat16 matrix cores (bf16x3.hip)
+// Operands split into three bfloat16 planes with k contiguous, K padded with
+// zeros to Kp (a multiple of 32): a = [3][M][Kp], b = [3][N][Kp].
+struct Bf16x3Args {
+  int M, N;
+  long Kp;
+  const unsigned short *a, *b;
+  long plane_a, plane_b;  // bfloat16 per plane: M * Kp, N * Kp
+  float *C;
+  long ldc;
+};
+
+// Split A (M x K, k along its columns) into wa = [3][M][Kp] and B (K x N, k
+// along its rows) into wb = [3][N][Kp] bfloat16 planes, in one launch.
+hipError_t launch_split(const float *A, long lda, const float *B, long ldb, int M, int N, int K,
+                        int Kp, void *wa, void *wb, hipStream_t stream);
+
+// C = sum of the six piece products over the planes.  hipErrorInvalidValue
+// if a slice's offsets do not fit a buffer descriptor.
+hipError_t launch_bf16x3_gemm(MfmaTile tile, const Bf16x3Args &p, hipStream_t stream);
+
+// One-instruction probe of the bfloat16 32x32x16 matrix instruction.
+hipError_t launch_bf16_probe(const float *A, const float *B, float *C, hipStream_t stream);
+
 // C[i] = A[i] + B[i], i < n (n >= 1).
 hipError_t launch_vector_add(long n, const float *A, const float *B, float *C,
                              hipStream_t stream);

@@ -165,12 +165,14 @@ int sgemm_run_strided_batched(int transA, int transB, int64_t M, int64_t N, int6
 
 /*
  * Matrix-core layout probe: one wave multiplies a 32 x 2 block of A by a
- * 2 x 32 block of B (which = 0, v_mfma_f32_32x32x2_f32) or a 16 x 4 block by
- * a 4 x 16 block (which = 1, v_mfma_f32_16x16x4_f32), with A and B row-major
- * and packed, and writes the 32 x 32 (or 16 x 16) product row-major and
- * packed to C.  It exercises the operand and accumulator lane maps that the
- * matrix-core kernels rely on.  SGEMM_ERR_INVALID_VALUE for another `which`
- * or a null pointer.
+ * 2 x 32 block of B (which = 0, v_mfma_f32_32x32x2_f32), a 16 x 4 block by
+ * a 4 x 16 block (which = 1, v_mfma_f32_16x16x4_f32), or a 32 x 16 block by
+ * a 16 x 32 block in bfloat16 (which = 2, v_mfma_f32_32x32x16_bf16; the
+ * high 16 bits of each float input are its bfloat16 value), with A and B
+ * row-major and packed, and writes the 32 x 32 (or 16 x 16) product
+ * row-major and packed to C.  It exercises the operand and accumulator lane
+ * maps that the matrix-core kernels rely on.  SGEMM_ERR_INVALID_VALUE for
+ * another `which` or a null pointer.
  */
 int sgemm_mfma_probe(int which, const float *A, const float *B, float *C, void *stream);
 

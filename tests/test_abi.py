@@ -28,7 +28,8 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = set(_declared_functions())
     for n in ("sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_run_variant",
-              "sgemm_run_ex", "sgemm_run_strided_batched", "vector_add", "sgemm_mfma_probe", "sgemm_status_string", "sgemm_variant_name"):
+              "sgemm_run_ex", "sgemm_run_strided_batched", "vector_add", "sgemm_mfma_probe",
+              "sgemm_bf16x3_workspace_size", "sgemm_run_bf16x3", "sgemm_status_string", "sgemm_variant_name"):
         assert n in names
 
 
@@ -75,7 +76,7 @@ def test_unknown_variant_rejected():
     lib = sg.load_library()
     rc = lib.sgemm_run_variant(sg.NUM_VARIANTS, 4, 4, 4, 1, 4, 1, 4, 1, 4, None)
     assert sg.sgemm_status_string(rc) == "SGEMM_ERR_INVALID_VALUE"
-    rc = lib.sgemm_mfma_probe(2, 1, 1, 1, None)
+    rc = lib.sgemm_mfma_probe(3, 1, 1, 1, None)
     assert sg.sgemm_status_string(rc) == "SGEMM_ERR_INVALID_VALUE"
 
 
@@ -135,3 +136,27 @@ def test_vector_add_host_side_argument_checks(n, ptr, status):
     lib = sg.load_library()
     rc = lib.vector_add(n, 1, ptr or None, 1, None)
     assert sg.sgemm_status_string(rc) == status
+
+
+def test_bf16x3_workspace_size_and_host_checks():
+    lib = sg.load_library()
+    assert lib.sgemm_bf16x3_workspace_size(100, 50, 33) == 6 * 64 * 150
+    assert lib.sgemm_bf16x3_workspace_size(100, 50, 0) == 0
+    assert sg.sgemm_status_string(lib.sgemm_bf16x3_workspace_size(-1, 5, 5)) == \
+        "SGEMM_ERR_INVALID_VALUE"
+    assert sg.sgemm_status_string(lib.sgemm_bf16x3_workspace_size(5, 5, 2 ** 21 + 1)) == \
+        "SGEMM_ERR_TOO_LARGE"
+    assert sg.sgemm_status_string(lib.sgemm_bf16x3_workspace_size(2 ** 30, 2 ** 30, 64)) == \
+        "SGEMM_ERR_TOO_LARGE"
+    need = lib.sgemm_bf16x3_workspace_size(4, 4, 4)
+    run = lib.sgemm_run_bf16x3
+    assert sg.sgemm_status_string(run(4, 4, 4, 16, 4, 16, 4, 16, 4, 256, need, None)) == \
+        "SGEMM_ERR_NOT_INITIALIZED"
+    assert sg.sgemm_status_string(run(4, 4, 4, 16, 4, 16, 4, 16, 4, 256, need - 1, None)) == \
+        "SGEMM_ERR_INVALID_VALUE"
+    assert sg.sgemm_status_string(run(4, 4, 4, 16, 4, 16, 4, 16, 4, 264, need, None)) == \
+        "SGEMM_ERR_INVALID_VALUE"
+    assert sg.sgemm_status_string(run(4, 4, 4, 16, 4, 16, 4, 16, 4, None, need, None)) == \
+        "SGEMM_ERR_INVALID_VALUE"
+    assert sg.sgemm_status_string(run(4, 4, 4, 16, 3, 16, 4, 16, 4, 256, need, None)) == \
+        "SGEMM_ERR_INVALID_VALUE"

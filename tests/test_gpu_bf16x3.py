@@ -1,0 +1,184 @@
+"""The product on the bfloat16 matrix cores (sgemm_run_bf16x3) against the
+oracle, through the C-ABI.
+
+* the split written to the workspace equals the oracle's three-piece split
+  bit for bit (A planes, and B's planes transposed, K padded with zeros);
+* the product meets the same tolerance as the single-precision path,
+  |C - Cref| <= 1e-5 * sum_k |A(i,k) B(k,j)| + 1e-6, with the same usage
+  bound, on the same workloads; at 8192^3 on 4096 sampled entries plus a
+  whole-matrix Freivalds check;
+* small-integer inputs (exact in the first piece) give exact products.
+"""
+import numpy as np
+import pytest
+
+import dense_fp32_matrix_03_amd as sg
+import oracle
+from dense_fp32_matrix_03_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def library():
+    sg.sgemm_create()
+    yield
+    sg.sgemm_destroy()
+
+
+def _dev(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _run(A, B, M, N, K, lda=None, ldb=None, ldc=None, keep_workspace=False):
+    import torch
+    lda = A.shape[1] if lda is None else lda
+    ldb = B.shape[1] if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    dA, dB = _dev(A), _dev(B)
+    dC = torch.full((max(M, 1), ldc), float("nan"), dtype=torch.float32, device="cuda")
+    nbytes = sg.sgemm_bf16x3_workspace_size(M, N, K)
+    ws = torch.full((max(nbytes, 16) // 2,), 0x7fff, dtype=torch.int16, device="cuda")
+    sg.sgemm_run_bf16x3(M, N, K, dA, lda, dB, ldb, dC, ldc, ws, nbytes)
+    torch.cuda.synchronize()
+    C = dC.cpu().numpy()[:M]
+    if keep_workspace:
+        return C, ws.cpu().numpy().view(np.uint16)
+    return C
+
+
+def test_bf16_probe_index_encoded():
+    """A(i,k) = i - 8 k, B(k,j) = 2 k - j: small integers, exact in bfloat16."""
+    import torch
+    A = np.array([[i - 8 * k for k in range(16)] for i in range(32)], dtype=np.float32)
+    B = np.array([[2 * k - j for j in range(32)] for k in range(16)], dtype=np.float32)
+    dC = torch.full((32, 32), float("nan"), dtype=torch.float32, device="cuda")
+    sg.sgemm_mfma_probe(2, _dev(A), _dev(B), dC)
+    torch.cuda.synchronize()
+    Cref, _ = oracle.sgemm_f64(A, B)
+    assert np.array_equal(dC.cpu().numpy().astype(np.float64), Cref)
+
+
+@pytest.mark.parametrize("M,N,K,lda", [(96, 80, 100, 100), (33, 70, 45, 47), (256, 128, 64, 64)])
+def test_workspace_holds_the_oracle_split(M, N, K, lda):
+    g = np.random.default_rng(M + N + K)
+    A = inputs.padded(inputs.normal(g, (M, K)), lda)
+    B = inputs.normal(g, (K, N))
+    _, ws = _run(A, B, M, N, K, lda=lda, keep_workspace=True)
+    Kp = (K + 31) // 32 * 32
+    nbytes = sg.sgemm_bf16x3_workspace_size(M, N, K)
+    assert nbytes == 6 * Kp * (M + N)
+    wa = ws[:3 * M * Kp].reshape(3, M, Kp)
+    wb = ws[3 * M * Kp:3 * (M + N) * Kp].reshape(3, N, Kp)
+    Az = np.zeros((M, Kp), np.float32)
+    Az[:, :K] = A[:, :K]
+    Bz = np.zeros((N, Kp), np.float32)
+    Bz[:, :K] = B.T
+    for pl, (pa, pb) in enumerate(zip(oracle.split_bf16x3(Az), oracle.split_bf16x3(Bz))):
+        assert np.array_equal(wa[pl], pa), f"A plane {pl}"
+        assert np.array_equal(wb[pl], pb), f"B plane {pl}"
+
+
+@pytest.mark.parametrize("w", inputs.WORKLOADS[:4], ids=lambda w: w.name)
+def test_workload_tolerance(w):
+    A, B = inputs.make_inputs(w)
+    C = _run(A, B, w.M, w.N, w.K, lda=w.lda, ldb=w.ldb, ldc=w.ldc)
+    Cref, Sabs = oracle.sgemm_f64(A, B, K=w.K, N=w.N)
+    r = oracle.check(C[:, :w.N], Cref, Sabs)
+    print(f"{w.name} bf16x3: {r}")
+    assert r.ok, str(r)
+    assert r.usage < 0.05, f"tolerance usage {r.usage} suggests a precision defect"
+
+
+@pytest.mark.parametrize("w", inputs.WORKLOADS[:4], ids=lambda w: w.name)
+def test_workload_integer_exact(w):
+    A, B = inputs.make_inputs(w, dist="int8range")
+    C = _run(A, B, w.M, w.N, w.K, lda=w.lda, ldb=w.ldb, ldc=w.ldc)
+    Cref, _ = oracle.sgemm_f64(A, B, K=w.K, N=w.N)
+    assert np.array_equal(C[:, :w.N].astype(np.float64), Cref)
+
+
+def test_8192_sampled_and_whole_matrix():
+    import torch
+    w = inputs.WORKLOADS[4]
+    A, B = inputs.make_inputs(w)
+    C = _run(A, B, w.M, w.N, w.K)
+    assert np.all(np.isfinite(C)), "an output entry was never written"
+    I, J = inputs.sample_indices(w.M, w.N, w.seed)
+    cref, sabs = oracle.entries_f64(A, B, I, J)
+    r = oracle.check(C[I, J], cref, sabs)
+    print(f"{w.name} bf16x3 sampled: {r}")
+    assert r.ok, str(r)
+    assert r.usage < 0.05
+    ok, usage = oracle.freivalds(A, B, C, inputs.sign_vector(w.N, w.seed))
+    print(f"{w.name} bf16x3 freivalds usage {usage:.3e}")
+    assert ok
+    del C
+    torch.cuda.empty_cache()
+
+
+EDGE = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 129, 255, 257, 300]
+
+
+def test_edge_sweep():
+    g0 = np.random.default_rng(211)
+    for _ in range(40):
+        M, N, K = (int(x) for x in g0.choice(EDGE, 3))
+        g = np.random.default_rng(M * 65536 + N * 256 + K)
+        A = inputs.uniform(g, (M, K))
+        B = inputs.uniform(g, (K, N))
+        C = _run(A, B, M, N, K)
+        Cref, Sabs = oracle.sgemm_f64(A, B)
+        r = oracle.check(C, Cref, Sabs)
+        assert r.ok, f"M={M} N={N} K={K}: {r}"
+
+
+def test_wide_exponent_range():
+    """Operands spread over 2^-40 .. 2^40 per row and column scale."""
+    g = np.random.default_rng(223)
+    M, N, K = 200, 160, 300
+    A = (inputs.normal(g, (M, K)) * np.exp2(g.integers(-40, 40, (M, 1)))).astype(np.float32)
+    B = (inputs.normal(g, (K, N)) * np.exp2(g.integers(-40, 40, (1, N)))).astype(np.float32)
+    C = _run(A, B, M, N, K)
+    Cref, Sabs = oracle.sgemm_f64(A, B)
+    r = oracle.check(C, Cref, Sabs)
+    assert r.ok, str(r)
+
+
+def test_padded_and_unaligned_leading_dimensions():
+    g = np.random.default_rng(227)
+    M, N, K = 130, 150, 170
+    A = inputs.padded(inputs.uniform(g, (M, K)), 173)
+    B = inputs.padded(inputs.uniform(g, (K, N)), 151)
+    C = _run(A, B, M, N, K, lda=173, ldb=151, ldc=157)
+    Cref, Sabs = oracle.sgemm_f64(A, B, K=K, N=N)
+    assert oracle.check(C[:, :N], Cref, Sabs).ok
+    assert np.all(np.isnan(C[:, N:])), "columns past N of C were written"
+
+
+def test_k_zero_and_empty():
+    import torch
+    dC = torch.full((5, 7), float("nan"), dtype=torch.float32, device="cuda")
+    d = torch.zeros(64, device="cuda")
+    assert sg.sgemm_bf16x3_workspace_size(5, 7, 0) == 0
+    sg.sgemm_run_bf16x3(5, 7, 0, d, 1, d, 7, dC, 7, None, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(dC.cpu().numpy(), np.zeros((5, 7), np.float32))
+    sg.sgemm_run_bf16x3(0, 7, 3, None, 3, None, 7, None, 7, None, 0)
+
+
+def test_workspace_errors():
+    import torch
+    d = torch.zeros(4096, device="cuda")
+    need = sg.sgemm_bf16x3_workspace_size(8, 8, 8)
+    assert need == 6 * 32 * 16
+    ws = torch.zeros(need // 4 + 8, device="cuda")
+    with pytest.raises(sg.SgemmError):  # too small
+        sg.sgemm_run_bf16x3(8, 8, 8, d, 8, d, 8, d, 8, ws, need - 1)
+    with pytest.raises(sg.SgemmError):  # misaligned
+        sg.sgemm_run_bf16x3(8, 8, 8, d, 8, d, 8, d, 8, ws.data_ptr() + 4, need)
+    with pytest.raises(sg.SgemmError):  # missing
+        sg.sgemm_run_bf16x3(8, 8, 8, d, 8, d, 8, d, 8, None, need)
+    sg.sgemm_run_bf16x3(8, 8, 8, d, 8, d, 8, d, 8, ws, need)
+    torch.cuda.synchronize()
