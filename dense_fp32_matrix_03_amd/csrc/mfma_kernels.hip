@@ -10,21 +10,25 @@ namespace sgemm {
 // Tile configurations (block tile, K slice, wave grid), from a sweep over
 // square problems of 1024 .. 8192 on MI355X:
 //   T256  256 x 256 x 32, 2 x 4 waves of 128 x 64  (two waves per SIMD)
-//   T128  128 x 128 x 32, 2 x 2 waves of  64 x 64
+//   T128  128 x 128 x 32, 4 x 2 waves of  32 x 64  (two waves per SIMD;
+//         the register-staged kernel keeps 2 x 2 waves of 64 x 64)
 //   T64    64 x  64 x 32, 2 x 2 waves of  32 x 32
+// At 2048^3 (one 128 x 128 tile per CU) eight waves instead of four took the
+// buffer-to-LDS kernel from 140.7 to 144.9 TFLOP/s; at 4096^3 both give 150.5.
 // WIDE_ONLY: only the 16-byte-load forms are instantiated (the caller
-// guarantees va && vb).
-template <int BM, int BN, int BK, int WM, int WN, bool WIDE_ONLY = false>
+// guarantees va && vb).  DWM x DWN: wave grid of the buffer-to-LDS kernel.
+template <int BM, int BN, int BK, int WM, int WN, bool WIDE_ONLY = false, int DWM = WM,
+          int DWN = WN>
 static hipError_t launch_tile(MfmaPath path, const GemmArgs &p, bool va, bool vb,
                               hipStream_t stream) {
   constexpr int kStoreGroup = 1;  // staged kernel: write the next slice after group 1 of 4
   const bool dma = dma_offsets_fit(BM, p.lda, BK, p.ldb);
   switch (path) {
     case MfmaPath::Auto:
-      if (dma) return launch_dma_cfg<BM, BN, BK, WM, WN, true, 1, WIDE_ONLY>(p, va, vb, stream);
+      if (dma) return launch_dma_cfg<BM, BN, BK, DWM, DWN, true, 1, WIDE_ONLY>(p, va, vb, stream);
       return launch_staged_cfg<BM, BN, BK, WM, WN, 4, kStoreGroup>(p, va, vb, stream);
     case MfmaPath::Unpadded:
-      if (dma) return launch_dma_cfg<BM, BN, BK, WM, WN, false, 1, WIDE_ONLY>(p, va, vb, stream);
+      if (dma) return launch_dma_cfg<BM, BN, BK, DWM, DWN, false, 1, WIDE_ONLY>(p, va, vb, stream);
       return launch_staged_cfg<BM, BN, BK, WM, WN, 0, kStoreGroup>(p, va, vb, stream);
     case MfmaPath::Staged:
       return launch_staged_cfg<BM, BN, BK, WM, WN, 4, kStoreGroup>(p, va, vb, stream);
@@ -51,9 +55,10 @@ hipError_t launch_mfma(MfmaTile tile, MfmaPath path, const GemmArgs &p, bool va,
     case MfmaTile::T256:
       // The 256 x 256 tile keeps 128 accumulators per lane; its 4-byte-load
       // forms would spill, so operands that need them take the 128 x 128 tile.
-      if (!(va && vb)) return launch_tile<128, 128, 32, 2, 2>(path, p, va, vb, stream);
+      if (!(va && vb)) return launch_tile<128, 128, 32, 2, 2, false, 4, 2>(path, p, va, vb, stream);
       return launch_tile<256, 256, 32, 2, 4, true>(path, p, va, vb, stream);
-    case MfmaTile::T128: return launch_tile<128, 128, 32, 2, 2>(path, p, va, vb, stream);
+    case MfmaTile::T128:
+      return launch_tile<128, 128, 32, 2, 2, false, 4, 2>(path, p, va, vb, stream);
     case MfmaTile::T64: return launch_tile<64, 64, 32, 2, 2>(path, p, va, vb, stream);
   }
   return hipErrorInvalidValue;
@@ -75,7 +80,7 @@ hipError_t launch_mfma_general(MfmaTile tile, const GemmArgs &p, bool ta, bool t
     return launch_dma_cfg<256, 256, 32, 2, 4, true, 1, true>(p, va, vb, stream);
   }
   if (tile == MfmaTile::T64) return launch_general_tile<64, 64, 32, 2, 2>(p, ta, tb, va, vb, stream);
-  return launch_general_tile<128, 128, 32, 2, 2>(p, ta, tb, va, vb, stream);
+  return launch_general_tile<128, 128, 32, 4, 2>(p, ta, tb, va, vb, stream);
 }
 
 // ---------------------------------------------------------------------------
