@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -63,7 +64,8 @@ def measured_traffic(workload: str):
     return c.get("hbm_bytes_per_launch")
 
 
-def time_gpu(w, variant: str, steps: int, warmup: int, warm_seconds: float = 0.0):
+def time_gpu(w, variant: str, steps: int, warmup: int, warm_seconds: float = 0.0,
+             trials: int = 1):
     import torch
 
     import dense_fp32_matrix_03_amd as sg
@@ -90,18 +92,58 @@ def time_gpu(w, variant: str, steps: int, warmup: int, warm_seconds: float = 0.0
         for _ in range(50):
             step()
         torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    per_trial = []
+    for _ in range(trials):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps):
+            step()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        per_trial.append(t0.elapsed_time(t1) / steps)
     finite = bool(torch.isfinite(dC[:, :w.N]).all().item())
     del dA, dB, dC
     torch.cuda.empty_cache()
-    return ms, finite
+    if trials == 1:
+        return per_trial[0], finite
+    return per_trial, finite
+
+
+def mfma_ceiling(which: int = 0, iters: int = 20000) -> float:
+    """TFLOP/s of the library's register-only matrix-core loop (which = 0:
+    FP32 32x32x2, 1: bfloat16 32x32x16), best of 5 launches after 2."""
+    import torch
+
+    import dense_fp32_matrix_03_amd as sg
+
+    out = torch.empty(1024 * torch.cuda.get_device_properties(0).multi_processor_count,
+                      dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = 0.0
+    for i in range(7):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        flops = sg.sgemm_mfma_ceiling(which, iters, out, out.numel(), stream.cuda_stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            best = max(best, flops / (t0.elapsed_time(t1) * 1e-3) / 1e12)
+    if not bool(torch.isfinite(out).all().item()):
+        raise RuntimeError("matrix-core ceiling loop produced non-finite sums")
+    return best
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(w, target_s: float = 12.0):
@@ -144,19 +186,33 @@ def oracle_seconds(w, threads: int, rows: int | None = None) -> tuple[float, int
 
 
 def workload_table(variant) -> list[dict]:
-    """GPU time of sgemm_run and oracle times, for every workload."""
+    """GPU time of sgemm_run (10 trials of R back-to-back calls, R = max(10,
+    200 ms / t); median and min) and oracle times, for every workload, with
+    the rate as a fraction of the published peak and of the measured
+    matrix-core ceiling."""
+    import statistics
+
     import oracle
     from dense_fp32_matrix_03_amd import inputs
 
     cores = oracle.max_threads()
+    ceiling = mfma_ceiling(0)
+    print(json.dumps({"mfma_ceiling_tflops": round(ceiling, 2),
+                      "pct_of_peak": round(100 * ceiling / PEAK_TFLOPS, 1),
+                      "host_cpu": cpu_model(), "host_threads": cores}), flush=True)
     rows = []
     rate1 = None
     for w in inputs.WORKLOADS:
-        reps = max(5, min(200, int(2e11 / w.flops) + 5))
-        ms, finite = time_gpu(w, variant, reps, 3, warm_seconds=0.3)
-        tf = w.flops / (ms * 1e-3) / 1e12
-        r = {"workload": w.name, "gpu_ms": round(ms, 5), "gpu_tflops": round(tf, 2),
-             "pct_of_peak": round(100 * tf / PEAK_TFLOPS, 1), "output_finite": finite,
+        ms0, _ = time_gpu(w, variant, 5, 3, warm_seconds=0.3)
+        reps = max(10, int(math.ceil(200.0 / ms0)))
+        trials, finite = time_gpu(w, variant, reps, 3, warm_seconds=0.3, trials=10)
+        med, best = statistics.median(trials), min(trials)
+        tf = w.flops / (med * 1e-3) / 1e12
+        r = {"workload": w.name, "trials": 10, "calls_per_trial": reps,
+             "gpu_ms_median": round(med, 5), "gpu_ms_min": round(best, 5),
+             "gpu_tflops": round(tf, 2), "gpu_tflops_best": round(w.flops / (best * 1e-3) / 1e12, 2),
+             "pct_of_peak": round(100 * tf / PEAK_TFLOPS, 1),
+             "pct_of_mfma_ceiling": round(100 * tf / ceiling, 1), "output_finite": finite,
              "cores": cores}
         if w.check == "full":
             t1, _ = oracle_seconds(w, 1)
@@ -281,6 +337,9 @@ def bf16x3_table(steps: int, warmup: int, settle: float) -> list[dict]:
     rows = []
     stream = torch.cuda.current_stream()
     h = stream.cuda_stream
+    ceiling = mfma_ceiling(1)
+    print(json.dumps({"bf16_mfma_ceiling_tflops": round(ceiling, 1),
+                      "pct_of_bf16_peak": round(100 * ceiling / BF16_PEAK_TFLOPS, 1)}), flush=True)
     for name in ("sgemm_1024x1024x1024_uniform_seed1", SECONDARY, HEADLINE):
         w = inputs.BY_NAME[name]
         A, B = inputs.make_inputs(w)
@@ -317,6 +376,7 @@ def bf16x3_table(steps: int, warmup: int, settle: float) -> list[dict]:
              "pct_of_fp32_peak": round(100 * tf / PEAK_TFLOPS, 1),
              "bf16_tflops": round(6 * tf, 1),
              "pct_of_bf16_peak": round(100 * 6 * tf / BF16_PEAK_TFLOPS, 1),
+             "pct_of_bf16_ceiling": round(100 * 6 * tf / ceiling, 1),
              "workspace_bytes": nbytes,
              "output_finite": bool(torch.isfinite(dC[:, :w.N]).all().item())}
         print(json.dumps(r), flush=True)

@@ -77,6 +77,8 @@ def load_library(path: str = LIB_PATH):
     lib.sgemm_run_bf16x3.restype = ci
     lib.vector_add.argtypes = [i64, vp, vp, vp, vp]
     lib.vector_add.restype = ci
+    lib.sgemm_mfma_ceiling.argtypes = [ci, ci, vp, i64, ctypes.POINTER(ctypes.c_double), vp]
+    lib.sgemm_mfma_ceiling.restype = ci
     lib.sgemm_mfma_probe.argtypes = [ci, vp, vp, vp, vp]
     lib.sgemm_mfma_probe.restype = ci
     lib.sgemm_status_string.argtypes = [ci]
@@ -170,6 +172,14 @@ def vector_add(n, A, B, C, stream=None) -> None:
     """C[i] = A[i] + B[i] for i < n (include/vector_add.h)."""
     _check("vector_add", load_library().vector_add(n, _ptr(A), _ptr(B), _ptr(C),
                                                    _stream(stream)))
+
+
+def sgemm_mfma_ceiling(which, iters, out, out_len, stream=None) -> float:
+    """Launch the register-only matrix-core loop; return its flop count."""
+    flops = ctypes.c_double(0.0)
+    _check("sgemm_mfma_ceiling", load_library().sgemm_mfma_ceiling(
+        int(which), int(iters), _ptr(out), int(out_len), ctypes.byref(flops), _stream(stream)))
+    return flops.value
 
 
 def sgemm_mfma_probe(which, A, B, C, stream=None) -> None:

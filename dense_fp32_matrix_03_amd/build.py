@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsgemm.so")
-SOURCES = ["api.hip", "mfma_kernels.hip", "valu_kernels.hip", "vector_add.hip", "bf16x3.hip"]
+SOURCES = ["api.hip", "mfma_kernels.hip", "valu_kernels.hip", "vector_add.hip", "bf16x3.hip",
+           "ceiling.hip"]
 ARCH = "gfx950"
 
 

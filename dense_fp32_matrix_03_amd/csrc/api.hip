@@ -327,6 +327,19 @@ int vector_add(int64_t n, const float *A, const float *B, float *C, void *stream
   return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 
+int sgemm_mfma_ceiling(int which, int iters, float *out, int64_t out_len, double *flops,
+                       void *stream) {
+  if ((which != 0 && which != 1) || iters < 1 || !out || !flops) return SGEMM_ERR_INVALID_VALUE;
+  if (!g_ready.load(std::memory_order_acquire)) return SGEMM_ERR_NOT_INITIALIZED;
+  DeviceInfo di;
+  const int rc = current_device_info(&di);
+  if (rc != SGEMM_OK) return rc;
+  if (out_len < sgemm::mfma_ceiling_outputs(di.cus)) return SGEMM_ERR_INVALID_VALUE;
+  const hipError_t err = sgemm::launch_mfma_ceiling(which, iters, out, di.cus, flops,
+                                                    reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
 const char *sgemm_status_string(int status) {
   switch (status) {
     case SGEMM_OK: return "SGEMM_OK";

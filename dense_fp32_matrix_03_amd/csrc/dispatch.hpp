@@ -68,6 +68,13 @@ hipError_t launch_bf16x3_gemm(MfmaTile tile, const Bf16x3Args &p, hipStream_t st
 // One-instruction probe of the bfloat16 32x32x16 matrix instruction.
 hipError_t launch_bf16_probe(const float *A, const float *B, float *C, hipStream_t stream);
 
+// Register-only matrix-core loop on every CU (which: 0 = FP32 32x32x2,
+// 1 = bfloat16 32x32x16); *flops receives the launch's flop count.  `out`
+// holds mfma_ceiling_outputs(cus) floats.
+long mfma_ceiling_outputs(int cus);
+hipError_t launch_mfma_ceiling(int which, int iters, float *out, int cus, double *flops,
+                               hipStream_t stream);
+
 // C[i] = A[i] + B[i], i < n (n >= 1).
 hipError_t launch_vector_add(long n, const float *A, const float *B, float *C,
                              hipStream_t stream);

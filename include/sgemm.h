@@ -176,6 +176,21 @@ int sgemm_run_strided_batched(int transA, int transB, int64_t M, int64_t N, int6
  */
 int sgemm_mfma_probe(int which, const float *A, const float *B, float *C, void *stream);
 
+/*
+ * Matrix-core ceiling: a register-only loop of `iters` iterations over eight
+ * independent accumulator chains per wave, four 256-thread work-groups per
+ * compute unit, on every compute unit of the current device, with no memory
+ * traffic; which = 0 times v_mfma_f32_32x32x2_f32, which = 1
+ * v_mfma_f32_32x32x16_bf16.  It measures the rate the matrix cores attain,
+ * against which a product kernel's rate is read beside the published peak.
+ * `out` is a device buffer of out_len floats that receives one sum per
+ * thread (at least 1024 per compute unit); *flops (host memory) receives the
+ * launch's flop count.  SGEMM_ERR_INVALID_VALUE for another `which`,
+ * iters < 1, a null pointer or a short `out`.
+ */
+int sgemm_mfma_ceiling(int which, int iters, float *out, int64_t out_len, double *flops,
+                       void *stream);
+
 /* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
 const char *sgemm_status_string(int status);
 

@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
     names = set(_declared_functions())
     for n in ("sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_run_variant",
               "sgemm_run_ex", "sgemm_run_strided_batched", "vector_add", "sgemm_mfma_probe",
-              "sgemm_bf16x3_workspace_size", "sgemm_run_bf16x3", "sgemm_status_string", "sgemm_variant_name"):
+              "sgemm_bf16x3_workspace_size", "sgemm_run_bf16x3", "sgemm_mfma_ceiling", "sgemm_status_string", "sgemm_variant_name"):
         assert n in names
 
 
@@ -160,3 +160,13 @@ def test_bf16x3_workspace_size_and_host_checks():
         "SGEMM_ERR_INVALID_VALUE"
     assert sg.sgemm_status_string(run(4, 4, 4, 16, 3, 16, 4, 16, 4, 256, need, None)) == \
         "SGEMM_ERR_INVALID_VALUE"
+
+
+def test_mfma_ceiling_host_checks():
+    lib = sg.load_library()
+    f = ctypes.c_double()
+    for which, iters, out in ((2, 10, 16), (0, 0, 16), (0, 10, 0)):
+        rc = lib.sgemm_mfma_ceiling(which, iters, out or None, 1 << 20, ctypes.byref(f), None)
+        assert sg.sgemm_status_string(rc) == "SGEMM_ERR_INVALID_VALUE"
+    rc = lib.sgemm_mfma_ceiling(0, 10, 16, 1 << 20, ctypes.byref(f), None)
+    assert sg.sgemm_status_string(rc) == "SGEMM_ERR_NOT_INITIALIZED"

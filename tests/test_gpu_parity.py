@@ -65,6 +65,20 @@ def test_mfma_probe_index_encoded(which, m, k):
     assert np.array_equal(dC.cpu().numpy().astype(np.float64), Cref)
 
 
+@pytest.mark.parametrize("which,per_instr", [(0, 2 * 32 * 32 * 2), (1, 2 * 32 * 32 * 16)])
+def test_mfma_ceiling_loop_runs(which, per_instr):
+    """The register-only ceiling loop: flop count and finite per-thread sums."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.full((1024 * cus,), float("nan"), dtype=torch.float32, device="cuda")
+    flops = sg.sgemm_mfma_ceiling(which, 50, out, out.numel())
+    torch.cuda.synchronize()
+    assert flops == per_instr * 8 * 50 * (4 * cus) * 4
+    assert bool(torch.isfinite(out).all().item())
+    with pytest.raises(sg.SgemmError):
+        sg.sgemm_mfma_ceiling(which, 50, out, out.numel() - 1)
+
+
 # -- the five workloads -----------------------------------------------------------
 
 @pytest.mark.parametrize("w", inputs.WORKLOADS[:4], ids=lambda w: w.name)
