@@ -332,3 +332,64 @@ def test_matmul_helper_and_streams():
     s.synchronize()
     Cref, Sabs = oracle.sgemm_f64(A, B)
     assert oracle.check(dC.cpu().numpy(), Cref, Sabs).ok
+
+
+def test_concurrent_streams():
+    """Products of different shapes (so different tiles) on four streams at
+    once, three rounds: the library keeps no per-call state."""
+    import torch
+    shapes = [(512, 384, 256), (1000, 1500, 777), (256, 256, 1024), (2048, 256, 64)]
+    g = np.random.default_rng(47)
+    cases = []
+    for M, N, K in shapes:
+        A = inputs.uniform(g, (M, K))
+        B = inputs.uniform(g, (K, N))
+        Cref, Sabs = oracle.sgemm_f64(A, B)
+        cases.append((M, N, K, _dev(A), _dev(B), Cref, Sabs))
+    streams = [torch.cuda.Stream() for _ in shapes]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        outs = []
+        for (M, N, K, dA, dB, _, _), s in zip(cases, streams):
+            with torch.cuda.stream(s):
+                dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+                for _ in range(4):
+                    sg.sgemm_run(M, N, K, dA, K, dB, N, dC, N, s)
+            outs.append(dC)
+        torch.cuda.synchronize()
+        for (M, N, K, _, _, Cref, Sabs), dC in zip(cases, outs):
+            r = oracle.check(dC.cpu().numpy(), Cref, Sabs)
+            assert r.ok, f"{M}x{N}x{K}: {r}"
+
+
+def test_leading_dimension_past_32_bit_offsets():
+    """lda = 2^30 + 8: a 64-row slice of A spans more than a buffer
+    descriptor's 2 GiB, so sgemm_run falls back to the register-staged kernel
+    (64-bit addressing); the general entry point reports SGEMM_ERR_TOO_LARGE
+    and the bfloat16-split path (which reads A in its own split kernel)
+    computes it."""
+    import torch
+    M, N, K, lda = 3, 48, 64, (1 << 30) + 8
+    g = np.random.default_rng(53)
+    A = inputs.uniform(g, (M, K))
+    B = inputs.uniform(g, (K, N))
+    big = torch.full(((M - 1) * lda + K,), float("nan"), dtype=torch.float32, device="cuda")
+    for i in range(M):
+        big[i * lda:i * lda + K] = torch.from_numpy(A[i]).cuda()
+    dB = _dev(B)
+    Cref, Sabs = oracle.sgemm_f64(A, B)
+    dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    sg.sgemm_run(M, N, K, big, lda, dB, N, dC, N)
+    torch.cuda.synchronize()
+    assert oracle.check(dC.cpu().numpy(), Cref, Sabs).ok
+    with pytest.raises(sg.SgemmError) as e:
+        sg.sgemm_run_ex(0, 0, M, N, K, 1.0, big, lda, dB, N, 0.0, dC, N)
+    assert e.value.status == sg._C["SGEMM_ERR_TOO_LARGE"]
+    nbytes = sg.sgemm_bf16x3_workspace_size(M, N, K)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dC.fill_(float("nan"))
+    sg.sgemm_run_bf16x3(M, N, K, big, lda, dB, N, dC, N, ws, nbytes)
+    torch.cuda.synchronize()
+    assert oracle.check(dC.cpu().numpy(), Cref, Sabs).ok
+    del big
+    torch.cuda.empty_cache()
