@@ -214,17 +214,6 @@ __device__ __forceinline__ int bf16_swizzle(int row) {
     return kc_swizzle<16, true>(row);
 }
 
-// Barrier that first retires all but this wave's N most recent
-// buffer-to-LDS loads: s_waitcnt vmcnt(N) (vmcnt is 6 bits, split over bits
-// 3:0 and 15:14 of SIMM16; expcnt and lgkmcnt at their "don't wait" maxima),
-// then the work-group barrier.
-template <int N>
-__device__ __forceinline__ void dma_barrier_keep() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xf << 8) | ((N >> 4) << 14));
-  __syncthreads();
-}
-
 // NS LDS stages: slice t lives in stage t % NS; the loads of slice t + NS
 // go out right after the barrier that ends slice t, so each load has NS - 1
 // slices of time to arrive.

@@ -79,6 +79,17 @@ __device__ __forceinline__ void dma_barrier() {
   __syncthreads();
 }
 
+// The same barrier, but retiring all except this wave's N most recent
+// buffer-to-LDS loads (s_waitcnt vmcnt(N); vmcnt is 6 bits, split over bits
+// 3:0 and 15:14 of SIMM16).  Loads retire in issue order, so with the loads
+// of the later slices as the N most recent, the earlier slices have landed.
+template <int N>
+__device__ __forceinline__ void dma_barrier_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xf << 8) | ((N >> 4) << 14));
+  __syncthreads();
+}
+
 // One wave-wide buffer-to-LDS load: lane l's 16 (WIDE) or 4 bytes at byte
 // offset `off` of the buffer land at LDS address lds + 16 l (or 4 l).
 template <bool WIDE>
@@ -327,7 +338,7 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
 
   dma(S0(), 0);
   dma(S1(), 1);
-  dma_barrier();
+  dma_barrier_keep<GA::NBW + GB::NBW>();  // slice 0 has landed; slice 1 may still fly
   read_ops(S0(), 0, cur);
   for (int t = 0; t < nk; t += 2) {
     slice(S0(), t);
