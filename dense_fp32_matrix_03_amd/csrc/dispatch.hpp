@@ -11,9 +11,9 @@ namespace sgemm {
 enum class MfmaTile { T256, T128, T64 };
 
 // Which matrix-core kernel:
-//  Auto      buffer-to-LDS loads when the operands allow them (16-byte
-//            aligned, ld % 4 == 0, K % 4 == 0, N % 4 == 0), else register
-//            staged;
+//  Auto      buffer-to-LDS loads (16 bytes per lane where va / vb, else
+//            4), or register-staged loads when a slice's offsets do not fit
+//            a buffer descriptor (a leading dimension near 2^29 or more);
 //  Staged    register-staged loads always;
 //  Unpadded  as Auto but without the LDS anti-conflict layout (no A swizzle,
 //            no A row padding), to measure what that layout buys.

@@ -68,17 +68,20 @@ extern "C" {
 /*
  * Kernel variants for sgemm_run_variant.  The first four are the pages'
  * progression on vector FMA units -- one thread per output (blog v1 Naive;
- * article "基础矩陣乘法"), LDS tiling (blog v2 Shared Memory Tiled; chapter
- * section 三), register tiling with 8x8 outputs per thread over 128x128x16
- * blocks (chapter sections 一 and 二), and that with a double-buffered LDS
- * pipeline (chapter section 四).  SGEMM_VARIANT_MFMA is the matrix-core
- * path that sgemm_run uses: 16-byte aligned operands with leading
- * dimensions, K and N multiples of 4 are fetched by buffer-to-LDS loads,
- * others through registers.  The _MFMA_<n> variants force its n x n block
- * tile instead of choosing one from the shape.  SGEMM_VARIANT_MFMA_STAGED
- * always fetches through registers, and SGEMM_VARIANT_MFMA_UNPADDED drops
- * the LDS anti-conflict layout (the chapter's padding, section 三): both
- * exist to measure what those steps are worth.
+ * the article's basic kernel, section "矩陣乘法基礎與CUDA實現原理"), LDS
+ * tiling (blog v2 Shared Memory Tiled; chapter section 三), register tiling
+ * with 8x8 outputs per thread over 128x128x16 blocks (chapter sections 一
+ * and 二), and that with a double-buffered LDS pipeline (chapter section
+ * 四).  SGEMM_VARIANT_MFMA is the matrix-core path that sgemm_run uses:
+ * operand slices reach LDS by buffer-to-LDS loads, 16 bytes per lane where
+ * the operand is 16-byte aligned with a leading dimension and width that are
+ * multiples of 4, else 4 bytes; only an operand whose leading dimension puts
+ * one slice beyond 2 GiB is fetched through registers instead.  The
+ * _MFMA_<n> variants force its n x n block tile instead of choosing one
+ * from the shape.  SGEMM_VARIANT_MFMA_STAGED always fetches through
+ * registers, and SGEMM_VARIANT_MFMA_UNPADDED drops the LDS anti-conflict
+ * layout (the chapter's padding, section 三): both exist to measure what
+ * those steps are worth.
  */
 #define SGEMM_VARIANT_NAIVE 0
 #define SGEMM_VARIANT_LDS 1
