@@ -11,6 +11,8 @@ What is here:
   double products A(i,k) * B(k,j), plus the sum of their absolute values.
   The definition is the summation formula of the article "硬件加速原理：CUDA核函数
   优化矩阵乘法的内存访问模式", section "矩阵乘法的计算特性".
+* ``entries_ex_f64`` -- selected entries of the general form, equal to
+  ``sgemm_ex_f64``'s entry by entry (for products too large to compute whole).
 * ``sgemm_ex_f64`` -- the general form C = alpha op(A) op(B) + beta C0 with
   optionally transposed operands; the same exact-product, ascending-k double
   sum, then alpha * sum + beta * C0, with scale |alpha| S + |beta| |C0|.
@@ -78,6 +80,10 @@ def _load():
                                         ctypes.c_double, fp, i64, fp, i64, ctypes.c_double,
                                         fp, i64, dp, i64, dp, i64, ctypes.c_int]
     lib.oracle_sgemm_ex_f64.restype = ctypes.c_int
+    lib.oracle_entries_ex_f64.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                                          ctypes.c_double, fp, i64, fp, i64, ctypes.c_double,
+                                          fp, i64, i64, fp, fp, dp, dp]
+    lib.oracle_entries_ex_f64.restype = ctypes.c_int
     lib.oracle_split_bf16x3.argtypes = [i64, fp, fp, fp, fp]
     lib.oracle_split_bf16x3.restype = ctypes.c_int
     lib.oracle_vector_add.argtypes = [i64, fp, fp, fp]
@@ -174,6 +180,33 @@ def entries_f64(A: np.ndarray, B: np.ndarray, I, J, K: int | None = None,
                                     _ptr(c), _ptr(s))
     if rc != 0:
         raise ValueError(f"oracle_entries_f64 rejected its arguments (rc={rc})")
+    return c, s
+
+
+def entries_ex_f64(transA: bool, transB: bool, M: int, N: int, K: int, alpha: float,
+                   A: np.ndarray, B: np.ndarray, I, J, beta: float = 0.0,
+                   C0: np.ndarray | None = None):
+    """(cref, sabs) of entries (I[e], J[e]) of alpha op(A) op(B) + beta C0;
+    storage as for sgemm_ex_f64.  Equal, entry by entry, to sgemm_ex_f64."""
+    A, lda = _as_f32(A, K if transA else M, M if transA else K, "A")
+    B, ldb = _as_f32(B, N if transB else K, K if transB else N, "B")
+    if beta != 0.0:
+        C0, ldc0 = _as_f32(C0, M, N, "C0")
+    else:
+        C0, ldc0 = None, max(1, N)
+    I = np.ascontiguousarray(I, dtype=np.int64)
+    J = np.ascontiguousarray(J, dtype=np.int64)
+    if I.shape != J.shape or I.ndim != 1:
+        raise ValueError("I and J must be 1-D and of equal length")
+    n = I.shape[0]
+    c = np.empty(n, dtype=np.float64)
+    s = np.empty(n, dtype=np.float64)
+    rc = _load().oracle_entries_ex_f64(int(transA), int(transB), M, N, K, float(alpha), _ptr(A),
+                                       lda, _ptr(B), ldb, float(beta),
+                                       _ptr(C0) if C0 is not None else None, ldc0, n, _ptr(I),
+                                       _ptr(J), _ptr(c), _ptr(s))
+    if rc != 0:
+        raise ValueError(f"oracle_entries_ex_f64 rejected its arguments (rc={rc})")
     return c, s
 
 

@@ -178,6 +178,42 @@ int oracle_sgemm_ex_f64(int transA, int transB, int64_t M, int64_t N, int64_t K,
 }
 
 /*
+ * Selected entries of the general form, for products too large to compute
+ * whole: entry e is (I[e], J[e]) of alpha op(A) op(B) + beta C0, with the same
+ * ascending-k double sum, the same final combination and the same scale as
+ * oracle_sgemm_ex_f64, so each entry equals that routine's bit for bit.
+ */
+int oracle_entries_ex_f64(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                          double alpha, const float *A, int64_t lda, const float *B,
+                          int64_t ldb, double beta, const float *C0, int64_t ldc0, int64_t n,
+                          const int64_t *I, const int64_t *J, double *cref, double *sabs)
+{
+    const int64_t acols = transA ? M : K, bcols = transB ? K : N;
+    if (M < 0 || N < 0 || K < 0 || n < 0) return ORACLE_BAD_ARG;
+    if (lda < (acols > 1 ? acols : 1) || ldb < (bcols > 1 ? bcols : 1)) return ORACLE_BAD_ARG;
+    if (beta != 0.0 && ldc0 < (N > 1 ? N : 1)) return ORACLE_BAD_ARG;
+    if (n == 0) return ORACLE_OK;
+    if (!I || !J || !cref || (K > 0 && (!A || !B)) || (beta != 0.0 && !C0)) return ORACLE_BAD_ARG;
+    for (int64_t e = 0; e < n; ++e)
+        if (I[e] < 0 || I[e] >= M || J[e] < 0 || J[e] >= N) return ORACLE_BAD_ARG;
+    for (int64_t e = 0; e < n; ++e) {
+        const int64_t i = I[e], j = J[e];
+        double c = 0.0, sa = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = (double)(transA ? A[k * lda + i] : A[i * lda + k]);
+            const double b = (double)(transB ? B[j * ldb + k] : B[k * ldb + j]);
+            const double prod = a * b;
+            c += prod;
+            sa += fabs(prod);
+        }
+        const double c0 = beta != 0.0 ? (double)C0[i * ldc0 + j] : 0.0;
+        cref[e] = alpha * c + beta * c0;
+        if (sabs) sabs[e] = fabs(alpha) * sa + fabs(beta) * fabs(c0);
+    }
+    return ORACLE_OK;
+}
+
+/*
  * Vector addition C[i] = A[i] + B[i], i = 0 .. n-1, in single precision
  * [blog "【infra之路】03_动手写 CUDA Kernel", 实验 1 (experiment 1), the
  * vector-addition kernel: one element per thread, one add].  The result is

@@ -515,3 +515,22 @@ def test_six_of_nine_products_meet_the_single_precision_bound():
     three = sum(px[i] * py[j] for i in range(3) for j in range(3) if i + j <= 1)
     assert np.max(np.abs(six - exact) / np.abs(exact)) < 2.0 ** -22
     assert np.max(np.abs(three - exact) / np.abs(exact)) > 1e-5
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False), (True, True)])
+def test_general_entries_equal_full_bitwise(ta, tb):
+    """The entry-wise general form equals the full routine bit for bit."""
+    g = np.random.default_rng(71 + 2 * ta + tb)
+    M, N, K = 23, 31, 40
+    A = inputs.normal(g, (K, M) if ta else (M, K))
+    B = inputs.normal(g, (N, K) if tb else (K, N))
+    C0 = inputs.normal(g, (M, N))
+    Cref, Sabs = oracle.sgemm_ex_f64(ta, tb, M, N, K, -0.75, A, B, 0.5, C0)
+    I, J = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    c, s = oracle.entries_ex_f64(ta, tb, M, N, K, -0.75, A, B, I.ravel(), J.ravel(), 0.5, C0)
+    assert np.array_equal(c, Cref.ravel()) and np.array_equal(s, Sabs.ravel())
+    c0, _ = oracle.entries_ex_f64(ta, tb, M, N, K, 2.0, A, B, [3], [4])
+    full0, _ = oracle.sgemm_ex_f64(ta, tb, M, N, K, 2.0, A, B)
+    assert c0[0] == full0[3, 4]
+    with pytest.raises(ValueError):
+        oracle.entries_ex_f64(ta, tb, M, N, K, 1.0, A, B, [M], [0])
