@@ -205,3 +205,61 @@ def test_general_argument_errors():
     with pytest.raises(sg.SgemmError):  # negative stride
         sg.sgemm_run_strided_batched(0, 0, 4, 4, 4, 1.0, d, 4, -1, d, 4, 0, 0.0, d, 4, 16, 2)
     sg.sgemm_run_strided_batched(0, 0, 4, 4, 4, 1.0, d, 4, 0, d, 4, 0, 0.0, d, 4, 16, 0)  # no-op
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS, ids=LAYOUT_IDS)
+def test_general_8192_sampled(ta, tb):
+    """The headline size in every layout, alpha = -0.75 and beta = 0.5: the
+    sampled entries of the 8192^3 workload against the oracle, plus every
+    entry finite."""
+    import torch
+    w = inputs.WORKLOADS[4]
+    M = N = K = w.M
+    g = np.random.default_rng(300 + 2 * int(ta) + int(tb))
+    A, B = _stored(g, ta, tb, M, N, K)
+    C0 = inputs.uniform(g, (M, N))
+    dA, dB, dC = _dev(A), _dev(B), _dev(C0)
+    sg.sgemm_run_ex(ta, tb, M, N, K, -0.75, dA, A.shape[1], dB, B.shape[1], 0.5, dC, N)
+    torch.cuda.synchronize()
+    C = dC.cpu().numpy()
+    del dA, dB, dC
+    torch.cuda.empty_cache()
+    assert np.all(np.isfinite(C))
+    I, J = inputs.sample_indices(M, N, w.seed)
+    cref, sabs = oracle.entries_ex_f64(ta, tb, M, N, K, -0.75, A, B, I, J, 0.5, C0)
+    r = oracle.check(C[I, J], cref, sabs)
+    print(f"8192 {LAYOUT_IDS[2 * int(ta) + int(tb)]}: {r}")
+    assert r.ok, str(r)
+    assert r.usage < 0.05
+
+
+@pytest.mark.parametrize("ta,tb", [(False, True), (True, False)], ids=["NT", "TN"])
+def test_strided_batched_medium(ta, tb):
+    """Six products of 1024 x 768 x 640 with padded strides and alpha/beta,
+    each checked whole against the oracle."""
+    import torch
+    M, N, K, batch = 1024, 768, 640, 6
+    g = np.random.default_rng(310 + int(ta))
+    ar, ac = (K, M) if ta else (M, K)
+    br, bc = (N, K) if tb else (K, N)
+    sA, sB, sC = ar * ac + 128, br * bc + 64, M * N + 32
+    A = [inputs.uniform(g, (ar, ac)) for _ in range(batch)]
+    B = [inputs.uniform(g, (br, bc)) for _ in range(batch)]
+    C0 = [inputs.uniform(g, (M, N)) for _ in range(batch)]
+    bufA = np.full(sA * batch, np.nan, np.float32)
+    bufB = np.full(sB * batch, np.nan, np.float32)
+    bufC = np.full(sC * batch, np.nan, np.float32)
+    for b in range(batch):
+        bufA[b * sA:b * sA + ar * ac] = A[b].ravel()
+        bufB[b * sB:b * sB + br * bc] = B[b].ravel()
+        bufC[b * sC:b * sC + M * N] = C0[b].ravel()
+    dA, dB, dC = _dev(bufA), _dev(bufB), _dev(bufC)
+    sg.sgemm_run_strided_batched(ta, tb, M, N, K, 1.25, dA, ac, sA, dB, bc, sB, -1.0, dC, N, sC,
+                                 batch)
+    torch.cuda.synchronize()
+    out = dC.cpu().numpy()
+    for b in range(batch):
+        Cref, Sabs = oracle.sgemm_ex_f64(ta, tb, M, N, K, 1.25, A[b], B[b], -1.0, C0[b])
+        r = oracle.check(out[b * sC:b * sC + M * N].reshape(M, N), Cref, Sabs)
+        assert r.ok, f"product {b}: {r}"
+        assert np.all(np.isnan(out[b * sC + M * N:(b + 1) * sC]))
