@@ -456,7 +456,8 @@ bf16x3_gemm_kernel(Bf16x3Args p, int tiles_m, int tiles_n, int group_m) {
       for (int e = 0; e < 16; ++e) {
         const int row = row0 + i * 32 + acc32_row(lane, e);
         const int col = col0 + j * 32;
-        if (full || (row < p.M && col < p.N)) p.C[(long)row * p.ldc + col] = acc[i][j][e];
+        if (full || (row < p.M && col < p.N))
+          __builtin_nontemporal_store(acc[i][j][e], p.C + (long)row * p.ldc + col);
       }
 }
 

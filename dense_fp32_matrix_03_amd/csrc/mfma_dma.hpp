@@ -352,7 +352,10 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   // of its 32x32 block; rows >= M and columns >= N are not stored.  C is read
   // only when beta != 0, and then a block's 16 values per lane are all loaded
   // before any of them is stored (a store could alias a later load, so the
-  // compiler would otherwise wait out each load's latency in turn).
+  // compiler would otherwise wait out each load's latency in turn).  Stores
+  // that do not follow a read of C are non-temporal: C is not read again by
+  // this kernel, and streaming it out instead of leaving it dirty in L2 took
+  // 2048^3 from 144.3 to 146.1 TFLOP/s (1024^3: 112.6 to 114.1).
   const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN + r32;
   const bool full = (m0 + BM <= p.M) && (n0 + BN <= p.N);
   const bool plain = p.alpha == 1.f && p.beta == 0.f;
@@ -367,11 +370,11 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
       if (plain) {
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (inside(e)) *at(e) = acc[i][j][e];
+          if (inside(e)) __builtin_nontemporal_store(acc[i][j][e], at(e));
       } else if (p.beta == 0.f) {
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (inside(e)) *at(e) = p.alpha * acc[i][j][e];
+          if (inside(e)) __builtin_nontemporal_store(p.alpha * acc[i][j][e], at(e));
       } else {
         float c[16];
 #pragma unroll
