@@ -534,3 +534,14 @@ def test_general_entries_equal_full_bitwise(ta, tb):
     assert c0[0] == full0[3, 4]
     with pytest.raises(ValueError):
         oracle.entries_ex_f64(ta, tb, M, N, K, 1.0, A, B, [M], [0])
+
+
+def test_cross_check_against_numpy_float64_product():
+    """A cross-check, not a pin: numpy's float64 product (another summation
+    order) agrees with the oracle to within double rounding of the sum."""
+    g = np.random.default_rng(81)
+    A = inputs.normal(g, (150, 333))
+    B = inputs.normal(g, (333, 170))
+    Cref, Sabs = oracle.sgemm_f64(A, B)
+    C64 = A.astype(np.float64) @ B.astype(np.float64)
+    assert np.max(np.abs(C64 - Cref) / Sabs) <= 333 * 2.0 ** -52
