@@ -10,7 +10,15 @@ as a width) fails at least one of them:
 * exact integer products compared with numpy's int64 matrix product;
 * invariants: padded leading dimensions give the packed result, the entry-wise
   routine (textbook i-j-k order) equals the full routine bit for bit;
-* the acceptance check and the whole-matrix check reject planted errors.
+* the acceptance check and the whole-matrix check reject planted errors;
+* the general form (transposes, alpha, beta): transposed storage gives the
+  plain bits, exact rationals over every layout, int64 exactness, and a
+  planted wrong transpose flag;
+* vector addition: the blog's sin^2 + cos^2 = 1 check and correct rounding
+  against exact rationals;
+* the bfloat16 split: exact reconstruction, nearest pieces against the
+  adjacent bfloat16 values, and the bound that fixes how many piece
+  products are kept.
 """
 import os
 
