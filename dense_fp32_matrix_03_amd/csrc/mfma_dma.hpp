@@ -35,7 +35,9 @@
 // Edges.  The buffer descriptor's range check turns a load at an offset
 // past num_records into zeros; an element outside op(A) (M x K) or op(B)
 // (K x N) is given such an offset, so ragged tiles and the K tail are
-// zero-filled by the hardware.  An operand that is 16-byte aligned with a
+// zero-filled by the hardware.  In the K-tail slice an operand whose k runs
+// along its stored rows needs no per-load test: num_records ends its window
+// after the last valid row.  An operand that is 16-byte aligned with a
 // leading dimension and a stored width that are multiples of 4 is fetched in
 // 16-byte chunks (64 lanes x 16 B = one 1 KiB block per instruction); any
 // other operand in single floats (256 B per instruction).
@@ -119,6 +121,7 @@ struct SliceGeom {
   static constexpr int NB = R * W / FPB;    // loads per slice
   static_assert(NB % NW == 0, "loads must split evenly over the waves");
   static constexpr int NBW = NB / NW;       // loads per wave per slice
+  static constexpr bool KR = KROWS;
 
   // Stored (row, col) of the window element that lane `lane` fetches in the
   // wave's q-th load: whichever element belongs at that lane's LDS position.
@@ -178,17 +181,20 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   // op(A)'s rows (M) or op(B)'s columns (N) get the out-of-range offset once
   // and for all; the K tail is handled per slice.
   unsigned offA[GA::NBW], offB[GB::NBW];
+  int kofA[GA::NBW], kofB[GB::NBW];  // k index of each load within a slice
 #pragma unroll
   for (int q = 0; q < GA::NBW; ++q) {
     int row, col;
     GA::elem(wave, lane, q, row, col);
     offA[q] = m0 + GA::mnof(row, col) < p.M ? (unsigned)(row * p.lda + col) * 4u : kOutOfRange;
+    kofA[q] = GA::kof(row, col);
   }
 #pragma unroll
   for (int q = 0; q < GB::NBW; ++q) {
     int row, col;
     GB::elem(wave, lane, q, row, col);
     offB[q] = n0 + GB::mnof(row, col) < p.N ? (unsigned)(row * p.ldb + col) * 4u : kOutOfRange;
+    kofB[q] = GB::kof(row, col);
   }
 
   // Issue the loads of slice t into LDS stage S.  A slice at or past the end
@@ -202,30 +208,28 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     float *bs = S.value ? Bs1 : Bs0;
     const int k0 = t < nk ? t * BK : 0;
     const int records = t < nk ? kBufferRecords : 0;
+    // K tail (not KFULL): an operand whose k runs along its stored rows ends
+    // its window after the last valid row, through the descriptor's
+    // num_records; the other operand compares each load's k index.
+    const int kl = p.K - k0 < BK ? p.K - k0 : BK;  // valid k in this slice
+    const int rec_a = KFULL || !GA::KR ? records : (t < nk ? kl * (int)p.lda * 4 : 0);
+    const int rec_b = KFULL || !GB::KR ? records : (t < nk ? kl * (int)p.ldb * 4 : 0);
     const float *abase = TA ? Ab + (long)k0 * p.lda + m0 : Ab + (long)m0 * p.lda + k0;
     const float *bbase = TB ? Bb + (long)n0 * p.ldb + k0 : Bb + (long)k0 * p.ldb + n0;
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(abase), 0, records, kRawBufferWord3);
+        const_cast<float *>(abase), 0, rec_a, kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(bbase), 0, records, kRawBufferWord3);
+        const_cast<float *>(bbase), 0, rec_b, kRawBufferWord3);
 #pragma unroll
     for (int q = 0; q < GA::NBW; ++q) {
       unsigned off = offA[q];
-      if constexpr (!KFULL) {
-        int row, col;
-        GA::elem(wave, lane, q, row, col);
-        off = k0 + GA::kof(row, col) < p.K ? off : kOutOfRange;
-      }
+      if constexpr (!KFULL && !GA::KR) off = kofA[q] < kl ? off : kOutOfRange;
       lds_dma<VA>(ra, as + (wave + q * NW) * GA::FPB, off);
     }
 #pragma unroll
     for (int q = 0; q < GB::NBW; ++q) {
       unsigned off = offB[q];
-      if constexpr (!KFULL) {
-        int row, col;
-        GB::elem(wave, lane, q, row, col);
-        off = k0 + GB::kof(row, col) < p.K ? off : kOutOfRange;
-      }
+      if constexpr (!KFULL && !GB::KR) off = kofB[q] < kl ? off : kOutOfRange;
       lds_dma<VB>(rb, bs + (wave + q * NW) * GB::FPB, off);
     }
   };
