@@ -328,7 +328,9 @@ def bf16x3_table(steps: int, warmup: int, settle: float) -> list[dict]:
     """Time sgemm_run_bf16x3 (split + product, one call) on the square
     workloads and report single-precision-equivalent TFLOP/s (2 M N K per
     call) next to the bfloat16 matrix-core rate of its six piece products
-    (6 * 2 M N K per call, whole call)."""
+    (6 * 2 M N K per call, whole call); then sgemm_run_bf16x3_ex with stored
+    transposes (alpha = 1, beta = 0) and with alpha / beta (no transposes)
+    at 2048^3 and 8192^3."""
     import torch
 
     import dense_fp32_matrix_03_amd as sg
@@ -340,19 +342,8 @@ def bf16x3_table(steps: int, warmup: int, settle: float) -> list[dict]:
     ceiling = mfma_ceiling(1)
     print(json.dumps({"bf16_mfma_ceiling_tflops": round(ceiling, 1),
                       "pct_of_bf16_peak": round(100 * ceiling / BF16_PEAK_TFLOPS, 1)}), flush=True)
-    for name in ("sgemm_1024x1024x1024_uniform_seed1", SECONDARY, HEADLINE):
-        w = inputs.BY_NAME[name]
-        A, B = inputs.make_inputs(w)
-        dA = torch.from_numpy(A).cuda()
-        dB = torch.from_numpy(B).cuda()
-        del A, B
-        dC = torch.empty((w.M, w.ldc), dtype=torch.float32, device="cuda")
-        nbytes = sg.sgemm_bf16x3_workspace_size(w.M, w.N, w.K)
-        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
 
-        def step():
-            sg.sgemm_run_bf16x3(w.M, w.N, w.K, dA, w.lda, dB, w.ldb, dC, w.ldc, ws, nbytes, h)
-
+    def timed(step, w):
         for _ in range(warmup):
             step()
         torch.cuda.synchronize()
@@ -369,9 +360,11 @@ def bf16x3_table(steps: int, warmup: int, settle: float) -> list[dict]:
             step()
         t1.record(stream)
         torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / n
+        return n, t0.elapsed_time(t1) / n
+
+    def report(w, n, ms, extra, dC, nbytes):
         tf = w.flops / (ms * 1e-3) / 1e12
-        r = {"kernel": "bf16x3", "workload": w.name, "steps": n, "ms": round(ms, 5),
+        r = {"kernel": "bf16x3", "workload": w.name, **extra, "steps": n, "ms": round(ms, 5),
              "tflops_fp32_equivalent": round(tf, 2),
              "pct_of_fp32_peak": round(100 * tf / PEAK_TFLOPS, 1),
              "bf16_tflops": round(6 * tf, 1),
@@ -381,6 +374,39 @@ def bf16x3_table(steps: int, warmup: int, settle: float) -> list[dict]:
              "output_finite": bool(torch.isfinite(dC[:, :w.N]).all().item())}
         print(json.dumps(r), flush=True)
         rows.append(r)
+
+    for name in ("sgemm_1024x1024x1024_uniform_seed1", SECONDARY, HEADLINE):
+        w = inputs.BY_NAME[name]
+        A, B = inputs.make_inputs(w)
+        dA = torch.from_numpy(A).cuda()
+        dB = torch.from_numpy(B).cuda()
+        del A, B
+        dC = torch.empty((w.M, w.ldc), dtype=torch.float32, device="cuda")
+        nbytes = sg.sgemm_bf16x3_workspace_size(w.M, w.N, w.K)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+        def step():
+            sg.sgemm_run_bf16x3(w.M, w.N, w.K, dA, w.lda, dB, w.ldb, dC, w.ldc, ws, nbytes, h)
+
+        n, ms = timed(step, w)
+        report(w, n, ms, {}, dC, nbytes)
+        if name != HEADLINE and name != SECONDARY:
+            del dA, dB, dC, ws
+            torch.cuda.empty_cache()
+            continue
+        # Square workloads: the stored transposes are the same arrays read
+        # the other way (uniform entries either way).
+        for ta, tb, alpha, beta in ((0, 1, 1.0, 0.0), (1, 0, 1.0, 0.0), (1, 1, 1.0, 0.0),
+                                    (0, 0, 1.5, 0.5)):
+            def step_ex(ta=ta, tb=tb, alpha=alpha, beta=beta):
+                sg.sgemm_run_bf16x3_ex(ta, tb, w.M, w.N, w.K, alpha, dA, w.lda, dB, w.ldb,
+                                       beta, dC, w.ldc, ws, nbytes, h)
+
+            dC.fill_(0.0)
+            n, ms = timed(step_ex, w)
+            layout = ("T" if ta else "N") + ("T" if tb else "N")
+            report(w, n, ms, {"entry": "sgemm_run_bf16x3_ex", "layout": layout,
+                              "alpha": alpha, "beta": beta}, dC, nbytes)
         del dA, dB, dC, ws
         torch.cuda.empty_cache()
     return rows

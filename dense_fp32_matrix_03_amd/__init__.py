@@ -75,6 +75,9 @@ def load_library(path: str = LIB_PATH):
     lib.sgemm_bf16x3_workspace_size.restype = i64
     lib.sgemm_run_bf16x3.argtypes = gemm_args[:-1] + [vp, i64, vp]
     lib.sgemm_run_bf16x3.restype = ci
+    lib.sgemm_run_bf16x3_ex.argtypes = [ci, ci, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp,
+                                        i64, vp, i64, vp]
+    lib.sgemm_run_bf16x3_ex.restype = ci
     lib.vector_add.argtypes = [i64, vp, vp, vp, vp]
     lib.vector_add.restype = ci
     lib.sgemm_mfma_ceiling.argtypes = [ci, ci, vp, i64, ctypes.POINTER(ctypes.c_double), vp]
@@ -166,6 +169,14 @@ def sgemm_run_bf16x3(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes
     _check("sgemm_run_bf16x3", load_library().sgemm_run_bf16x3(
         M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(workspace), workspace_bytes,
         _stream(stream)))
+
+
+def sgemm_run_bf16x3_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                        workspace, workspace_bytes, stream=None) -> None:
+    """C = alpha op(A) op(B) + beta C on the bfloat16 matrix cores."""
+    _check("sgemm_run_bf16x3_ex", load_library().sgemm_run_bf16x3_ex(
+        int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
+        float(beta), _ptr(C), ldc, _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def vector_add(n, A, B, C, stream=None) -> None:

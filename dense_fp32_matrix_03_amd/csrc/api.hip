@@ -249,41 +249,56 @@ int64_t sgemm_bf16x3_workspace_size(int64_t M, int64_t N, int64_t K) {
   return 6 * Kp * (M + N);  // three 2-byte planes of each operand
 }
 
-int sgemm_run_bf16x3(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
-                     const float *B, int64_t ldb, float *C, int64_t ldc, void *workspace,
-                     int64_t workspace_bytes, void *stream) {
-  int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc);
-  if (rc != SGEMM_OK) return rc;
-  const int64_t need = sgemm_bf16x3_workspace_size(M, N, K);
-  if (need < 0) return (int)need;
-  if (M > 0 && N > 0 && K > 0 &&
-      (!workspace || !aligned16(workspace) || workspace_bytes < need))
+int sgemm_run_bf16x3_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                        const float *A, int64_t lda, const float *B, int64_t ldb, float beta,
+                        float *C, int64_t ldc, void *workspace, int64_t workspace_bytes,
+                        void *stream) {
+  if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1)) return SGEMM_ERR_INVALID_VALUE;
+  if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_INVALID_VALUE;
+  const int64_t a_cols = transA ? M : K, b_cols = transB ? K : N;
+  if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1) ||
+      ldc < (N > 1 ? N : 1))
+    return SGEMM_ERR_INVALID_VALUE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return SGEMM_ERR_TOO_LARGE;
+  if (!grid_fits(M, N, 1, 64, 256)) return SGEMM_ERR_TOO_LARGE;
+  const bool reads_ab = M > 0 && N > 0 && K > 0 && alpha != 0.f;
+  int64_t need = 0;
+  if (reads_ab) {
+    need = sgemm_bf16x3_workspace_size(M, N, K);
+    if (need < 0) return (int)need;
+  }
+  if (M > 0 && N > 0 && !C) return SGEMM_ERR_INVALID_VALUE;
+  if (reads_ab && (!A || !B)) return SGEMM_ERR_INVALID_VALUE;
+  if (reads_ab && (!workspace || !aligned16(workspace) || workspace_bytes < need))
     return SGEMM_ERR_INVALID_VALUE;
   if (!g_ready.load(std::memory_order_acquire)) return SGEMM_ERR_NOT_INITIALIZED;
   if (M == 0 || N == 0) return SGEMM_OK;
   DeviceInfo di;
-  rc = current_device_info(&di);
+  const int rc = current_device_info(&di);
   if (rc != SGEMM_OK) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   hipError_t err;
-  if (K == 0) {
+  if (!reads_ab) {
     sgemm::GemmArgs z;
     z.M = (int)M;
     z.N = (int)N;
-    z.K = 0;
+    z.K = (int)K;
     z.A = A;
     z.lda = lda;
     z.B = B;
     z.ldb = ldb;
     z.C = C;
     z.ldc = ldc;
-    err = sgemm::launch_scale(z, s);  // the empty sum
+    z.alpha = alpha;
+    z.beta = beta;
+    err = sgemm::launch_scale(z, s);  // C = beta C (zeros when beta == 0)
   } else {
     const int64_t Kp = (K + 31) / 32 * 32;
     unsigned short *wa = static_cast<unsigned short *>(workspace);
     unsigned short *wb = wa + 3 * M * Kp;
-    err = sgemm::launch_split(A, lda, B, ldb, (int)M, (int)N, (int)K, (int)Kp, wa, wb, s);
+    err = sgemm::launch_split(transA != 0, transB != 0, A, lda, B, ldb, (int)M, (int)N, (int)K,
+                              (int)Kp, wa, wb, s);
     if (err == hipSuccess) {
       sgemm::Bf16x3Args p;
       p.M = (int)M;
@@ -295,11 +310,20 @@ int sgemm_run_bf16x3(int64_t M, int64_t N, int64_t K, const float *A, int64_t ld
       p.plane_b = N * Kp;
       p.C = C;
       p.ldc = ldc;
+      p.alpha = alpha;
+      p.beta = beta;
       err = sgemm::launch_bf16x3_gemm(sgemm::choose_mfma_tile(M, N, di.cus), p, s);
       if (err == hipErrorInvalidValue) return SGEMM_ERR_TOO_LARGE;
     }
   }
   return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+int sgemm_run_bf16x3(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                     const float *B, int64_t ldb, float *C, int64_t ldc, void *workspace,
+                     int64_t workspace_bytes, void *stream) {
+  return sgemm_run_bf16x3_ex(0, 0, M, N, K, 1.f, A, lda, B, ldb, 0.f, C, ldc, workspace,
+                             workspace_bytes, stream);
 }
 
 int sgemm_mfma_probe(int which, const float *A, const float *B, float *C, void *stream) {

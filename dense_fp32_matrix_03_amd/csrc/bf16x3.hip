@@ -71,66 +71,71 @@ __device__ __forceinline__ void split8(const float v[8], u32x4 out[3]) {
 
 // ------------------------------------------------------------------ split
 // One launch splits both operands: work-groups [0, blocks_a) take A, the
-// rest take B.
+// rest take B.  Each operand is split one of two ways, by where its k runs:
 //
-// A (k along its columns, M x K, leading dimension lda): one thread per 8
-// consecutive k of one row, k >= K read as 0.  VA: 16-byte aligned base and
-// lda % 4 == 0, so the 8 values come in two 16-byte loads where they lie
-// inside the row.
+// k along the stored columns (A as given, B transposed; rows x K, leading
+// dimension ld): one thread per 8 consecutive k of one row, k >= K read as 0.
+// VEC: 16-byte aligned base and ld % 4 == 0, so the 8 values come in two
+// 16-byte loads where they lie inside the row.
 //
-// B (k along its rows, K x N, leading dimension ldb), written transposed as
-// [N][Kp]: a 64 (k) x 64 (n) tile goes through LDS (rows read as 16 float4
-// per k row where VB: 16-byte aligned, ldb % 4 == 0, N % 4 == 0); then lane l
-// of each group of 8 takes k-chunk l % 8 of one column, so 8 lanes write 128
-// contiguous bytes of a plane row.
+// k along the stored rows (B as given, A transposed; K x cols), written
+// transposed as [cols][Kp]: a 64 (k) x 64 (column) tile goes through LDS
+// (read as 16 float4 per k row where VEC: 16-byte aligned, ld % 4 == 0,
+// cols % 4 == 0); then lane l of each group of 8 takes k-chunk l % 8 of one
+// column, so 8 lanes write 128 contiguous bytes of a plane row.
 constexpr int kSplitT = 64;
 
-struct SplitArgs {
-  const float *A;
-  long lda;
-  const float *B;
-  long ldb;
-  int M, N, K, Kp;
-  u32x4 *wa, *wb;  // plane 0 of A's and of B's planes (16-byte chunks)
-  long blocks_a;
-  int tiles_n;
+struct SplitOperand {
+  const float *X;
+  long ld;
+  int rows;     // rows of the planes: M for A, N for B
+  bool kcols;   // k runs along the stored columns
+  u32x4 *w;     // plane 0 (16-byte chunks); planes are rows * Kp / 8 chunks apart
+  long blocks;  // work-groups of this operand
+  int tiles_c;  // k-along-rows split: 64-column tiles
 };
 
-template <bool VA, bool VB>
-__global__ void __launch_bounds__(256) split_kernel(SplitArgs p) {
-  __shared__ float tile[kSplitT][kSplitT + 1];
-  const int tid = threadIdx.x;
-  const int cpr = p.Kp / 8;
-  if ((long)blockIdx.x < p.blocks_a) {
-    const long plane = (long)p.M * cpr;
-    const long q = (long)blockIdx.x * 256 + tid;
-    if (q >= plane) return;
-    const int row = (int)(q / cpr), c = (int)(q % cpr);
-    const int k0 = c * 8;
-    const float *x = p.A + (long)row * p.lda + k0;
-    float v[8];
-    if (VA && k0 + 8 <= p.K) {
-      const f32x4 lo = *reinterpret_cast<const f32x4 *>(x);
-      const f32x4 hi = *reinterpret_cast<const f32x4 *>(x + 4);
+struct SplitArgs {
+  SplitOperand a, b;
+  int K, Kp;
+};
+
+template <bool VEC>
+__device__ __forceinline__ void split_kcols_part(const SplitOperand &o, int K, int Kp, long blk) {
+  const int cpr = Kp / 8;
+  const long plane = (long)o.rows * cpr;
+  const long q = blk * 256 + threadIdx.x;
+  if (q >= plane) return;
+  const int row = (int)(q / cpr), c = (int)(q % cpr);
+  const int k0 = c * 8;
+  const float *x = o.X + (long)row * o.ld + k0;
+  float v[8];
+  if (VEC && k0 + 8 <= K) {
+    const f32x4 lo = *reinterpret_cast<const f32x4 *>(x);
+    const f32x4 hi = *reinterpret_cast<const f32x4 *>(x + 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = lo[e];
-        v[4 + e] = hi[e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = k0 + e < p.K ? x[e] : 0.f;
+    for (int e = 0; e < 4; ++e) {
+      v[e] = lo[e];
+      v[4 + e] = hi[e];
     }
-    u32x4 out[3];
-    split8(v, out);
+  } else {
 #pragma unroll
-    for (int pl = 0; pl < 3; ++pl) p.wa[pl * plane + q] = out[pl];
-    return;
+    for (int e = 0; e < 8; ++e) v[e] = k0 + e < K ? x[e] : 0.f;
   }
-  const long b = (long)blockIdx.x - p.blocks_a;
-  const int tn = (int)(b % p.tiles_n), tk = (int)(b / p.tiles_n);
+  u32x4 out[3];
+  split8(v, out);
+#pragma unroll
+  for (int pl = 0; pl < 3; ++pl) o.w[pl * plane + q] = out[pl];
+}
+
+template <bool VEC>
+__device__ __forceinline__ void split_krows_part(const SplitOperand &o, int K, int Kp, long blk,
+                                                 float (*tile)[kSplitT + 1]) {
+  const int tid = threadIdx.x;
+  const int cols = o.rows;
+  const int tn = (int)(blk % o.tiles_c), tk = (int)(blk / o.tiles_c);
   const int n0 = tn * kSplitT, k0 = tk * kSplitT;
-  if constexpr (VB) {
+  if constexpr (VEC) {
     // 64 rows x 16 float4: 4 per thread.
 #pragma unroll
     for (int i = 0; i < kSplitT * kSplitT / 4 / 256; ++i) {
@@ -138,7 +143,7 @@ __global__ void __launch_bounds__(256) split_kernel(SplitArgs p) {
       const int r = f / (kSplitT / 4), c4 = (f % (kSplitT / 4)) * 4;
       const int k = k0 + r, n = n0 + c4;
       f32x4 t = {0.f, 0.f, 0.f, 0.f};
-      if (k < p.K && n < p.N) t = *reinterpret_cast<const f32x4 *>(p.B + (long)k * p.ldb + n);
+      if (k < K && n < cols) t = *reinterpret_cast<const f32x4 *>(o.X + (long)k * o.ld + n);
 #pragma unroll
       for (int e = 0; e < 4; ++e) tile[r][c4 + e] = t[e];
     }
@@ -147,17 +152,18 @@ __global__ void __launch_bounds__(256) split_kernel(SplitArgs p) {
     for (int i = 0; i < kSplitT * kSplitT / 256; ++i) {
       const int r = tid / kSplitT + i * (256 / kSplitT), c = tid % kSplitT;
       const int k = k0 + r, n = n0 + c;
-      tile[r][c] = (k < p.K && n < p.N) ? p.B[(long)k * p.ldb + n] : 0.f;
+      tile[r][c] = (k < K && n < cols) ? o.X[(long)k * o.ld + n] : 0.f;
     }
   }
   __syncthreads();
-  const long plane = (long)p.N * cpr;
+  const int cpr = Kp / 8;
+  const long plane = (long)cols * cpr;
 #pragma unroll
   for (int i = 0; i < kSplitT * (kSplitT / 8) / 256; ++i) {
     const int task = tid + i * 256;
     const int kc = task % 8, c = task / 8;
     const int n = n0 + c, kchunk = k0 / 8 + kc;
-    if (n >= p.N || kchunk >= cpr) continue;
+    if (n >= cols || kchunk >= cpr) continue;
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = tile[kc * 8 + e][c];
@@ -165,29 +171,54 @@ __global__ void __launch_bounds__(256) split_kernel(SplitArgs p) {
     split8(v, out);
     const long q = (long)n * cpr + kchunk;
 #pragma unroll
-    for (int pl = 0; pl < 3; ++pl) p.wb[pl * plane + q] = out[pl];
+    for (int pl = 0; pl < 3; ++pl) o.w[pl * plane + q] = out[pl];
   }
 }
 
-hipError_t launch_split(const float *A, long lda, const float *B, long ldb, int M, int N, int K,
-                        int Kp, void *wa, void *wb, hipStream_t stream) {
+template <bool VA, bool VB>
+__global__ void __launch_bounds__(256) split_kernel(SplitArgs p) {
+  __shared__ float tile[kSplitT][kSplitT + 1];
+  const long blk = blockIdx.x;
+  // Which operand and which kind are uniform over the work-group.
+  if (blk < p.a.blocks) {
+    if (p.a.kcols)
+      split_kcols_part<VA>(p.a, p.K, p.Kp, blk);
+    else
+      split_krows_part<VA>(p.a, p.K, p.Kp, blk, tile);
+  } else {
+    if (p.b.kcols)
+      split_kcols_part<VB>(p.b, p.K, p.Kp, blk - p.a.blocks);
+    else
+      split_krows_part<VB>(p.b, p.K, p.Kp, blk - p.a.blocks, tile);
+  }
+}
+
+static SplitOperand split_operand(const float *X, long ld, int rows, bool kcols, int Kp,
+                                  void *w, bool &vec) {
+  SplitOperand o;
+  o.X = X;
+  o.ld = ld;
+  o.rows = rows;
+  o.kcols = kcols;
+  o.w = reinterpret_cast<u32x4 *>(w);
+  o.tiles_c = (rows + kSplitT - 1) / kSplitT;
+  if (kcols)
+    o.blocks = ((long)rows * (Kp / 8) + 255) / 256;
+  else
+    o.blocks = (long)o.tiles_c * ((Kp + kSplitT - 1) / kSplitT);
+  vec = (reinterpret_cast<uintptr_t>(X) & 15u) == 0 && ld % 4 == 0 && (kcols || rows % 4 == 0);
+  return o;
+}
+
+hipError_t launch_split(bool ta, bool tb, const float *A, long lda, const float *B, long ldb,
+                        int M, int N, int K, int Kp, void *wa, void *wb, hipStream_t stream) {
   SplitArgs p;
-  p.A = A;
-  p.lda = lda;
-  p.B = B;
-  p.ldb = ldb;
-  p.M = M;
-  p.N = N;
+  bool va, vb;
+  p.a = split_operand(A, lda, M, !ta, Kp, wa, va);
+  p.b = split_operand(B, ldb, N, tb, Kp, wb, vb);
   p.K = K;
   p.Kp = Kp;
-  p.wa = reinterpret_cast<u32x4 *>(wa);
-  p.wb = reinterpret_cast<u32x4 *>(wb);
-  p.blocks_a = ((long)M * (Kp / 8) + 255) / 256;
-  p.tiles_n = (N + kSplitT - 1) / kSplitT;
-  const long blocks_b = (long)p.tiles_n * ((Kp + kSplitT - 1) / kSplitT);
-  const dim3 grid((unsigned)(p.blocks_a + blocks_b)), block(256);
-  const bool va = (reinterpret_cast<uintptr_t>(A) & 15u) == 0 && lda % 4 == 0;
-  const bool vb = (reinterpret_cast<uintptr_t>(B) & 15u) == 0 && ldb % 4 == 0 && N % 4 == 0;
+  const dim3 grid((unsigned)(p.a.blocks + p.b.blocks)), block(256);
   if (va && vb)
     hipLaunchKernelGGL((split_kernel<true, true>), grid, block, 0, stream, p);
   else if (va)
@@ -446,19 +477,37 @@ bf16x3_gemm_kernel(Bf16x3Args p, int tiles_m, int tiles_n, int group_m) {
   // let them retire before the work-group gives up its LDS.
   __builtin_amdgcn_s_waitcnt(0x0f70);
 
+  // Epilogue as in the FP32 kernel: C is read only when beta != 0 (a
+  // block's 16 values per lane all loaded before any store); other stores
+  // are non-temporal.
   const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN + r32;
   const bool full = (m0 + BM <= p.M) && (n0 + BN <= p.N);
+  const bool plain = p.alpha == 1.f && p.beta == 0.f;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int j = 0; j < FN; ++j) {
+      const int col = col0 + j * 32;
+      auto row = [&](int e) { return row0 + i * 32 + acc32_row(lane, e); };
+      auto inside = [&](int e) { return full || (row(e) < p.M && col < p.N); };
+      auto at = [&](int e) { return p.C + (long)row(e) * p.ldc + col; };
+      if (plain) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = row0 + i * 32 + acc32_row(lane, e);
-        const int col = col0 + j * 32;
-        if (full || (row < p.M && col < p.N))
-          __builtin_nontemporal_store(acc[i][j][e], p.C + (long)row * p.ldc + col);
+        for (int e = 0; e < 16; ++e)
+          if (inside(e)) __builtin_nontemporal_store(acc[i][j][e], at(e));
+      } else if (p.beta == 0.f) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (inside(e)) __builtin_nontemporal_store(p.alpha * acc[i][j][e], at(e));
+      } else {
+        float c[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) c[e] = inside(e) ? *at(e) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (inside(e)) *at(e) = fmaf(p.alpha, acc[i][j][e], p.beta * c[e]);
       }
+    }
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int MODE, int NS>

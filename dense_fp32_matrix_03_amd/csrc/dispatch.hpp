@@ -54,14 +54,16 @@ struct Bf16x3Args {
   long plane_a, plane_b;  // bfloat16 per plane: M * Kp, N * Kp
   float *C;
   long ldc;
+  float alpha = 1.f, beta = 0.f;  // C = alpha (product) + beta C; C read only if beta != 0
 };
 
-// Split A (M x K, k along its columns) into wa = [3][M][Kp] and B (K x N, k
-// along its rows) into wb = [3][N][Kp] bfloat16 planes, in one launch.
-hipError_t launch_split(const float *A, long lda, const float *B, long ldb, int M, int N, int K,
-                        int Kp, void *wa, void *wb, hipStream_t stream);
+// Split op(A) (M x K) into wa = [3][M][Kp] and op(B) (K x N) into wb =
+// [3][N][Kp] bfloat16 planes, in one launch; ta / tb: A / B stored
+// transposed (A as K x M with leading dimension lda, B as N x K).
+hipError_t launch_split(bool ta, bool tb, const float *A, long lda, const float *B, long ldb,
+                        int M, int N, int K, int Kp, void *wa, void *wb, hipStream_t stream);
 
-// C = sum of the six piece products over the planes.  hipErrorInvalidValue
+// C = alpha (sum of the six piece products over the planes) + beta C.  hipErrorInvalidValue
 // if a slice's offsets do not fit a buffer descriptor.
 hipError_t launch_bf16x3_gemm(MfmaTile tile, const Bf16x3Args &p, hipStream_t stream);
 

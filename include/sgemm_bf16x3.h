@@ -22,9 +22,10 @@
  * Workspace.  The caller supplies device memory of at least
  * sgemm_bf16x3_workspace_size(M, N, K) bytes, 16-byte aligned.  A call
  * writes the split operands there -- with Kp = K rounded up to a multiple
- * of 32: A as three planes [3][M][Kp] of bfloat16 (k contiguous), then B
- * transposed as [3][N][Kp], padding columns zero -- and reads them back in
- * the product.  The contents are only meaningful until the next call that
+ * of 32: op(A) as three planes [3][M][Kp] of bfloat16 (k contiguous), then
+ * op(B) transposed as [3][N][Kp], padding columns zero; the planes are the
+ * same whichever way an operand is stored -- and reads them back in the
+ * product.  The contents are only meaningful until the next call that
  * uses the same workspace; two calls in flight on different streams must not
  * share one.  The library allocates nothing.
  *
@@ -33,6 +34,16 @@
  * errors: SGEMM_ERR_INVALID_VALUE for a null, misaligned or too small
  * workspace when M, N and K are all positive; SGEMM_ERR_TOO_LARGE for
  * K > 2^21 or (M + N) * Kp > 2^34.
+ *
+ * sgemm_run_bf16x3_ex is the general form of sgemm_run_ex (sgemm.h) on the
+ * same split: C = alpha * op(A) op(B) + beta * C with the transposes, the
+ * leading-dimension rules, the alpha == 0 / beta == 0 behaviour and the
+ * rounding of alpha * sum + beta * C of sgemm_run_ex, and the accuracy
+ * contract above for the sum.  The workspace is needed, and the workspace
+ * errors and size limits apply, only when M, N and K are positive and
+ * alpha != 0 (otherwise A, B and the workspace are not touched).
+ * sgemm_run_bf16x3 is sgemm_run_bf16x3_ex(0, 0, M, N, K, 1, A, lda, B, ldb,
+ * 0, C, ldc, ...).
  */
 #ifndef SGEMM_BF16X3_H_
 #define SGEMM_BF16X3_H_
@@ -55,6 +66,11 @@ int sgemm_run_bf16x3(int64_t M, int64_t N, int64_t K,
                      const float *B, int64_t ldb,
                      float *C, int64_t ldc,
                      void *workspace, int64_t workspace_bytes, void *stream);
+
+int sgemm_run_bf16x3_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                        const float *A, int64_t lda, const float *B, int64_t ldb, float beta,
+                        float *C, int64_t ldc, void *workspace, int64_t workspace_bytes,
+                        void *stream);
 
 #ifdef __cplusplus
 }

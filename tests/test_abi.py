@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     names = set(_declared_functions())
     for n in ("sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_run_variant",
               "sgemm_run_ex", "sgemm_run_strided_batched", "vector_add", "sgemm_mfma_probe",
-              "sgemm_bf16x3_workspace_size", "sgemm_run_bf16x3", "sgemm_mfma_ceiling", "sgemm_status_string", "sgemm_variant_name"):
+              "sgemm_bf16x3_workspace_size", "sgemm_run_bf16x3", "sgemm_run_bf16x3_ex",
+              "sgemm_mfma_ceiling", "sgemm_status_string", "sgemm_variant_name"):
         assert n in names
 
 
@@ -160,6 +161,53 @@ def test_bf16x3_workspace_size_and_host_checks():
         "SGEMM_ERR_INVALID_VALUE"
     assert sg.sgemm_status_string(run(4, 4, 4, 16, 3, 16, 4, 16, 4, 256, need, None)) == \
         "SGEMM_ERR_INVALID_VALUE"
+
+
+def test_bf16x3_ex_host_checks():
+    lib = sg.load_library()
+    ex = lib.sgemm_run_bf16x3_ex
+
+    def st(*args):
+        return sg.sgemm_status_string(ex(*args))
+
+    # (transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ws, ws_bytes, stream)
+    M, N, K = 6, 5, 3
+    need = lib.sgemm_bf16x3_workspace_size(M, N, K)
+    assert st(0, 0, M, N, K, 1, 16, K, 16, N, 0, 16, N, 256, need, None) == \
+        "SGEMM_ERR_NOT_INITIALIZED"
+    assert st(2, 0, M, N, K, 1, 16, K, 16, N, 0, 16, N, 256, need, None) == \
+        "SGEMM_ERR_INVALID_VALUE"
+    assert st(0, -1, M, N, K, 1, 16, K, 16, N, 0, 16, N, 256, need, None) == \
+        "SGEMM_ERR_INVALID_VALUE"
+    # Leading dimensions follow the stored shapes: A^T is K x M, B^T is N x K.
+    assert st(1, 0, M, N, K, 1, 16, K, 16, N, 0, 16, N, 256, need, None) == \
+        "SGEMM_ERR_INVALID_VALUE"
+    assert st(1, 0, M, N, K, 1, 16, M, 16, N, 0, 16, N, 256, need, None) == \
+        "SGEMM_ERR_NOT_INITIALIZED"
+    assert st(0, 1, M, N, K, 1, 16, K, 16, K - 1, 0, 16, N, 256, need, None) == \
+        "SGEMM_ERR_INVALID_VALUE"
+    assert st(0, 1, M, N, K, 1, 16, K, 16, K, 0, 16, N, 256, need, None) == \
+        "SGEMM_ERR_NOT_INITIALIZED"
+    assert st(0, 0, M, N, K, 1, 16, K, 16, N, 0, 16, N - 1, 256, need, None) == \
+        "SGEMM_ERR_INVALID_VALUE"
+    # The workspace is checked only when the product is formed.
+    assert st(0, 0, M, N, K, 1, 16, K, 16, N, 0, 16, N, 256, need - 1, None) == \
+        "SGEMM_ERR_INVALID_VALUE"
+    assert st(0, 0, M, N, K, 1, 16, K, 16, N, 0, 16, N, 264, need, None) == \
+        "SGEMM_ERR_INVALID_VALUE"
+    assert st(0, 0, M, N, K, 0, None, K, None, N, 2, 16, N, None, 0, None) == \
+        "SGEMM_ERR_NOT_INITIALIZED"
+    assert st(0, 0, M, N, 0, 1, None, 1, None, N, 2, 16, N, None, 0, None) == \
+        "SGEMM_ERR_NOT_INITIALIZED"
+    assert st(0, 0, M, N, K, 1, None, K, 16, N, 0, 16, N, 256, need, None) == \
+        "SGEMM_ERR_INVALID_VALUE"
+    assert st(0, 0, M, N, K, 1, 16, K, 16, N, 0, None, N, 256, need, None) == \
+        "SGEMM_ERR_INVALID_VALUE"
+    # Size limits of the split apply only when the product is formed.
+    assert st(0, 0, M, N, 2 ** 21 + 1, 1, 16, 2 ** 21 + 1, 16, N, 0, 16, N, 256, 1 << 40,
+              None) == "SGEMM_ERR_TOO_LARGE"
+    assert st(0, 0, M, N, 2 ** 21 + 1, 0, 16, 2 ** 21 + 1, 16, N, 0, 16, N, None, 0,
+              None) == "SGEMM_ERR_NOT_INITIALIZED"
 
 
 def test_mfma_ceiling_host_checks():
