@@ -324,13 +324,13 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bfloat16 matrix peak, published
 
 
-def bf16x3_table(steps: int, warmup: int, settle: float) -> list[dict]:
+def bf16x3_table(steps: int, warmup: int, settle: float, general: bool = False) -> list[dict]:
     """Time sgemm_run_bf16x3 (split + product, one call) on the square
     workloads and report single-precision-equivalent TFLOP/s (2 M N K per
     call) next to the bfloat16 matrix-core rate of its six piece products
-    (6 * 2 M N K per call, whole call); then sgemm_run_bf16x3_ex with stored
-    transposes (alpha = 1, beta = 0) and with alpha / beta (no transposes)
-    at 2048^3 and 8192^3."""
+    (6 * 2 M N K per call, whole call).  general: instead, at 2048^3 and
+    8192^3, sgemm_run_bf16x3_ex with stored transposes (alpha = 1, beta = 0)
+    and with alpha / beta (no transposes)."""
     import torch
 
     import dense_fp32_matrix_03_amd as sg
@@ -375,7 +375,9 @@ def bf16x3_table(steps: int, warmup: int, settle: float) -> list[dict]:
         print(json.dumps(r), flush=True)
         rows.append(r)
 
-    for name in ("sgemm_1024x1024x1024_uniform_seed1", SECONDARY, HEADLINE):
+    names = (SECONDARY, HEADLINE) if general else ("sgemm_1024x1024x1024_uniform_seed1",
+                                                   SECONDARY, HEADLINE)
+    for name in names:
         w = inputs.BY_NAME[name]
         A, B = inputs.make_inputs(w)
         dA = torch.from_numpy(A).cuda()
@@ -388,15 +390,15 @@ def bf16x3_table(steps: int, warmup: int, settle: float) -> list[dict]:
         def step():
             sg.sgemm_run_bf16x3(w.M, w.N, w.K, dA, w.lda, dB, w.ldb, dC, w.ldc, ws, nbytes, h)
 
-        n, ms = timed(step, w)
-        report(w, n, ms, {}, dC, nbytes)
-        if name != HEADLINE and name != SECONDARY:
+        if not general:
+            n, ms = timed(step, w)
+            report(w, n, ms, {}, dC, nbytes)
             del dA, dB, dC, ws
             torch.cuda.empty_cache()
             continue
         # Square workloads: the stored transposes are the same arrays read
         # the other way (uniform entries either way).
-        for ta, tb, alpha, beta in ((0, 1, 1.0, 0.0), (1, 0, 1.0, 0.0), (1, 1, 1.0, 0.0),
+        for ta, tb, alpha, beta in ((0, 1, 1.0, 0.0), (1, 1, 1.0, 0.0), (1, 0, 1.0, 0.0),
                                     (0, 0, 1.5, 0.5)):
             def step_ex(ta=ta, tb=tb, alpha=alpha, beta=beta):
                 sg.sgemm_run_bf16x3_ex(ta, tb, w.M, w.N, w.K, alpha, dA, w.lda, dB, w.ldb,
@@ -498,6 +500,9 @@ def main(argv=None) -> int:
     ap.add_argument("--bf16x3", action="store_true",
                     help="time sgemm_run_bf16x3 (single precision on the bfloat16 matrix "
                          "cores) at 1024^3, 2048^3 and 8192^3, one JSON line each")
+    ap.add_argument("--bf16x3-general", action="store_true",
+                    help="time sgemm_run_bf16x3_ex (stored transposes; alpha/beta) at "
+                         "2048^3 and 8192^3, one JSON line each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -534,8 +539,8 @@ def main(argv=None) -> int:
         workload_table(variant)
         sg.sgemm_destroy()
         return 0
-    if a.bf16x3:
-        bf16x3_table(a.steps, a.warmup, a.settle)
+    if a.bf16x3 or a.bf16x3_general:
+        bf16x3_table(a.steps, a.warmup, a.settle, general=a.bf16x3_general)
         sg.sgemm_destroy()
         return 0
     if a.vector_add:
