@@ -134,6 +134,23 @@ def test_edge_sweep():
         assert r.ok, f"M={M} N={N} K={K}: {r}"
 
 
+@pytest.mark.parametrize("shape", [(1, 1, 1 << 21), (2, 3, 1 << 20), (1 << 20, 3, 7),
+                                   (5, 1 << 20, 9), (4097, 4099, 1), (1 << 15, 1 << 9, 4)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_extreme_aspect_ratios(shape):
+    """Up to the longest K the split accepts (2^21), skinny and K = 1 shapes."""
+    M, N, K = shape
+    g = np.random.default_rng(M * 7 + N * 3 + K)
+    A = inputs.uniform(g, (M, K))
+    B = inputs.uniform(g, (K, N))
+    print(f"bf16x3 M={M} N={N} K={K}", flush=True)
+    C = _run(A, B, M, N, K)
+    Cref, Sabs = oracle.sgemm_f64(A, B)
+    r = oracle.check(C, Cref, Sabs)
+    assert r.ok, f"M={M} N={N} K={K}: {r}"
+    assert r.usage < 0.05, f"tolerance usage {r.usage}"
+
+
 def test_wide_exponent_range():
     """Operands spread over 2^-40 .. 2^40 per row and column scale."""
     g = np.random.default_rng(223)

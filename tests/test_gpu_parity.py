@@ -199,6 +199,27 @@ def test_edge_shape_sweep(variant):
         assert r.ok, f"{variant} M={M} N={N} K={K}: {r}"
 
 
+# Extreme aspect ratios: a 4M-long dot product, tall and wide skinny products,
+# an outer product (K = 1) and many tiles over a tiny K.
+EXTREME_SHAPES = [(1, 1, 1 << 22), (2, 3, 1 << 20), (1 << 20, 3, 7), (5, 1 << 20, 9),
+                  (4097, 4099, 1), (1 << 15, 1 << 9, 4)]
+
+
+@pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged"])
+@pytest.mark.parametrize("shape", EXTREME_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_extreme_aspect_ratios(variant, shape):
+    M, N, K = shape
+    g = np.random.default_rng(M * 7 + N * 3 + K)
+    A = inputs.uniform(g, (M, K))
+    B = inputs.uniform(g, (K, N))
+    print(f"{variant} M={M} N={N} K={K}", flush=True)
+    C = _run(A, B, M, N, K, variant=variant)
+    Cref, Sabs = oracle.sgemm_f64(A, B)
+    r = oracle.check(C, Cref, Sabs)
+    assert r.ok, f"{variant} M={M} N={N} K={K}: {r}"
+    assert r.usage < 0.05, f"tolerance usage {r.usage}"
+
+
 # Dimensions that are multiples of 4 (so the buffer-to-LDS path is taken) but
 # of no tile size: ragged M/N tiles and a ragged last K slice.
 DMA_DIMS = [4, 8, 12, 28, 36, 60, 68, 124, 132, 252, 260, 516]
