@@ -97,19 +97,33 @@ __global__ void __launch_bounds__(kRT) regtile_kernel(GemmArgs p, int tiles_n) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
 
+  // The operand vectors of step k + 1 are read from LDS before the 64 FMAs
+  // of step k, so their latency hides behind arithmetic even with one wave
+  // per SIMD.
+  struct Frag {
+    f32x4 a0, a1, b0, b1;
+  };
+  auto read_frag = [&](int s, int k, Frag &f) {
+    f.a0 = *reinterpret_cast<const f32x4 *>(&sAt[s][k * SAT + 4 * ty]);
+    f.a1 = *reinterpret_cast<const f32x4 *>(&sAt[s][k * SAT + 64 + 4 * ty]);
+    f.b0 = *reinterpret_cast<const f32x4 *>(&sB[s][k * kRB + 4 * tx]);
+    f.b1 = *reinterpret_cast<const f32x4 *>(&sB[s][k * kRB + 64 + 4 * tx]);
+  };
   auto compute_slice = [&](int s) {
+    Frag cur, nxt;
+    read_frag(s, 0, cur);
 #pragma unroll
     for (int k = 0; k < kRK; ++k) {
-      const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&sAt[s][k * SAT + 4 * ty]);
-      const f32x4 a1 = *reinterpret_cast<const f32x4 *>(&sAt[s][k * SAT + 64 + 4 * ty]);
-      const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&sB[s][k * kRB + 4 * tx]);
-      const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&sB[s][k * kRB + 64 + 4 * tx]);
-      float a[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      float b[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      if (k + 1 < kRK) read_frag(s, k + 1, nxt);
+      const float a[8] = {cur.a0[0], cur.a0[1], cur.a0[2], cur.a0[3],
+                          cur.a1[0], cur.a1[1], cur.a1[2], cur.a1[3]};
+      const float b[8] = {cur.b0[0], cur.b0[1], cur.b0[2], cur.b0[3],
+                          cur.b1[0], cur.b1[1], cur.b1[2], cur.b1[3]};
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+      cur = nxt;
     }
   };
 
@@ -132,15 +146,18 @@ __global__ void __launch_bounds__(kRT) regtile_kernel(GemmArgs p, int tiles_n) {
     store_slice(0);
     __syncthreads();
     for (int t = 0; t < nk; ++t) {
-      const bool more = t + 1 < nk;
-      if (more) {
-        fa.advance(0, kRK);
-        fb.advance(kRK, 0);
-        fa.load(p.M, p.K);
-        fb.load(p.K, p.N);
-      }
+      // Slice t + 1 into registers; past K the fetch reads nothing and
+      // yields zeros, which land in the stage no one reads again.  Issued
+      // before slice t's arithmetic, stored to LDS after it: the sched
+      // barrier keeps the compiler from moving the LDS stores (and with
+      // them the wait for the loads) above the arithmetic.
+      fa.advance(0, kRK);
+      fb.advance(kRK, 0);
+      fa.load(p.M, p.K);
+      fb.load(p.K, p.N);
       compute_slice(t & 1);
-      if (more) store_slice((t + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      store_slice((t + 1) & 1);
       __syncthreads();
     }
   }
