@@ -17,30 +17,38 @@ namespace {
 constexpr int kMaxDevices = 64;
 
 struct DeviceInfo {
-  bool known = false;
   bool supported = false;
   int cus = 0;
+};
+
+// One cached entry per device: `known` is set (release) after `info` is
+// filled, so a call that sees it set reads `info` without the lock.
+struct DeviceSlot {
+  std::atomic<bool> known{false};
+  DeviceInfo info;
 };
 
 std::mutex g_mu;
 int g_refs = 0;
 std::atomic<int> g_ready{0};
-DeviceInfo g_dev[kMaxDevices];
+DeviceSlot g_dev[kMaxDevices];
 
 // Query (once) and cache what the dispatcher needs to know about device d.
 int device_info(int d, DeviceInfo *out) {
   if (d < 0 || d >= kMaxDevices) return SGEMM_ERR_UNSUPPORTED_DEVICE;
-  std::lock_guard<std::mutex> lk(g_mu);
-  DeviceInfo &di = g_dev[d];
-  if (!di.known) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, d) != hipSuccess) return SGEMM_ERR_HIP;
-    di.supported = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-    di.cus = prop.multiProcessorCount;
-    di.known = true;
+  DeviceSlot &slot = g_dev[d];
+  if (!slot.known.load(std::memory_order_acquire)) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!slot.known.load(std::memory_order_relaxed)) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, d) != hipSuccess) return SGEMM_ERR_HIP;
+      slot.info.supported = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+      slot.info.cus = prop.multiProcessorCount;
+      slot.known.store(true, std::memory_order_release);
+    }
   }
-  *out = di;
-  return di.supported ? SGEMM_OK : SGEMM_ERR_UNSUPPORTED_DEVICE;
+  *out = slot.info;
+  return out->supported ? SGEMM_OK : SGEMM_ERR_UNSUPPORTED_DEVICE;
 }
 
 int current_device_info(DeviceInfo *out) {

@@ -17,10 +17,12 @@
 // Two passes:
 //  1. split: each operand is read once from HBM and written to the caller's
 //     workspace as three bfloat16 planes with k contiguous, K padded with
-//     zeros to Kp (a multiple of 32): A as [3][M][Kp], B transposed as
-//     [3][N][Kp].  Memory-bound, like the vector add.
+//     zeros to Kp (a multiple of 32): op(A) as [3][M][Kp], op(B) transposed
+//     as [3][N][Kp], whichever way each operand is stored.  Memory-bound,
+//     like the vector add.
 //  2. product: the buffer-to-LDS pipeline of the FP32 kernel (mfma_dma.hpp)
-//     over the six planes, v_mfma_f32_32x32x16_bf16 on 32 x 32 blocks.
+//     over the six planes, v_mfma_f32_32x32x16_bf16 on 32 x 32 blocks, and
+//     the FP32 kernel's alpha / beta epilogue.
 #include "common.hpp"
 #include "dispatch.hpp"
 #include "mfma_dma.hpp"

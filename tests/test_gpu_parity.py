@@ -383,6 +383,51 @@ def test_concurrent_streams():
             assert r.ok, f"{M}x{N}x{K}: {r}"
 
 
+def test_host_threads():
+    """Four host threads, each with its own stream, call sgemm_run (ctypes
+    drops the GIL for the call) on different shapes; every result equals the
+    single-threaded result bit for bit, and that one meets the oracle."""
+    import threading
+
+    import torch
+    shapes = [(512, 384, 256), (1000, 1500, 777), (256, 256, 1024), (2048, 256, 64)]
+    g = np.random.default_rng(59)
+    cases = []
+    for M, N, K in shapes:
+        A = inputs.uniform(g, (M, K))
+        B = inputs.uniform(g, (K, N))
+        ref = _run(A, B, M, N, K)
+        Cref, Sabs = oracle.sgemm_f64(A, B)
+        assert oracle.check(ref, Cref, Sabs).ok
+        cases.append((M, N, K, _dev(A), _dev(B), ref))
+    torch.cuda.synchronize()
+    errors = []
+    results = [None] * len(cases)
+
+    def worker(i):
+        try:
+            M, N, K, dA, dB, _ = cases[i]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+            for _ in range(25):
+                sg.sgemm_run(M, N, K, dA, K, dB, N, dC, N, s)
+            s.synchronize()
+            results[i] = dC.cpu().numpy()
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
+    for (M, N, K, _, _, ref), out in zip(cases, results):
+        assert out.tobytes() == ref.tobytes(), f"{M}x{N}x{K}"
+
+
 def test_leading_dimension_past_32_bit_offsets():
     """lda = 2^30 + 8: a 64-row slice of A spans more than a buffer
     descriptor's 2 GiB, so sgemm_run falls back to the register-staged kernel
