@@ -40,35 +40,29 @@ __device__ __forceinline__ f32x16 mfma32x32x16_bf16(bf16x8 a, bf16x8 b, f32x16 c
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// bfloat16 bit pattern of the float nearest to x with 8 significant bits,
-// ties to even (x finite): adding 0x7fff plus the lowest kept bit to the
-// float's bits carries into the kept half exactly when the dropped half is
-// above one half, or one half with an odd kept half.
-__device__ __forceinline__ unsigned rne_bf16_bits(float x) {
-  const unsigned u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ float bf16_bits_value(unsigned h) { return __uint_as_float(h << 16); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Split 8 floats into three 16-byte chunks of bfloat16 (element e in the
-// low half of word e/2 for even e).
+// low half of word e/2 for even e).  Each conversion is gfx950's
+// v_cvt_pk_bf16_f32 (two floats to their nearest bfloat16 values, ties to
+// even, in the default rounding mode); widening a bfloat16 back to float is
+// exact, and so is each residual: x minus its nearest 8-bit value needs at
+// most 16 significant bits, and that residual minus its own nearest 8-bit
+// value at most 8.
 __device__ __forceinline__ void split8(const float v[8], u32x4 out[3]) {
-  unsigned h[3][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const unsigned h0 = rne_bf16_bits(v[e]);
-    const float r1 = v[e] - bf16_bits_value(h0);  // exact
-    const unsigned h1 = rne_bf16_bits(r1);
-    const float r2 = r1 - bf16_bits_value(h1);    // exact, at most 8 significant bits
-    h[0][e] = h0;
-    h[1][e] = h1;
-    h[2][e] = rne_bf16_bits(r2);
+  for (int w = 0; w < 4; ++w) {
+    const f32x2 x = {v[2 * w], v[2 * w + 1]};
+    const bf16x2 h0 = __builtin_convertvector(x, bf16x2);
+    const f32x2 r1 = x - __builtin_convertvector(h0, f32x2);
+    const bf16x2 h1 = __builtin_convertvector(r1, bf16x2);
+    const f32x2 r2 = r1 - __builtin_convertvector(h1, f32x2);
+    const bf16x2 h2 = __builtin_convertvector(r2, bf16x2);
+    out[0][w] = __builtin_bit_cast(unsigned, h0);
+    out[1][w] = __builtin_bit_cast(unsigned, h1);
+    out[2][w] = __builtin_bit_cast(unsigned, h2);
   }
-#pragma unroll
-  for (int p = 0; p < 3; ++p)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) out[p][w] = (h[p][2 * w] & 0xffffu) | (h[p][2 * w + 1] << 16);
 }
 
 // ------------------------------------------------------------------ split
@@ -77,8 +71,11 @@ __device__ __forceinline__ void split8(const float v[8], u32x4 out[3]) {
 //
 // k along the stored columns (A as given, B transposed; rows x K, leading
 // dimension ld): one thread per 8 consecutive k of one row, k >= K read as 0.
-// VEC: 16-byte aligned base and ld % 4 == 0, so the 8 values come in two
-// 16-byte loads where they lie inside the row.
+// A work-group covers 256 / CW rows by CW such chunks (CW = 2^lcw, the
+// chunks per row rounded up to a power of two, at most 64), so a thread's
+// row and chunk come from shifts of its index.  VEC: 16-byte aligned base
+// and ld % 4 == 0, so the 8 values come in two 16-byte loads where they lie
+// inside the row.
 //
 // k along the stored rows (B as given, A transposed; K x cols), written
 // transposed as [cols][Kp]: a 64 (k) x 64 (column) tile goes through LDS
@@ -95,6 +92,8 @@ struct SplitOperand {
   u32x4 *w;     // plane 0 (16-byte chunks); planes are rows * Kp / 8 chunks apart
   long blocks;  // work-groups of this operand
   int tiles_c;  // k-along-rows split: 64-column tiles
+  int lcw;      // k-along-columns split: log2 of the chunks per work-group row
+  int groups_c; // k-along-columns split: work-groups across one row's chunks
 };
 
 struct SplitArgs {
@@ -106,9 +105,12 @@ template <bool VEC>
 __device__ __forceinline__ void split_kcols_part(const SplitOperand &o, int K, int Kp, long blk) {
   const int cpr = Kp / 8;
   const long plane = (long)o.rows * cpr;
-  const long q = blk * 256 + threadIdx.x;
-  if (q >= plane) return;
-  const int row = (int)(q / cpr), c = (int)(q % cpr);
+  const int by = (int)(blk / o.groups_c), bx = (int)(blk % o.groups_c);  // uniform
+  const int tid = threadIdx.x;
+  const int row = (by << (8 - o.lcw)) + (tid >> o.lcw);
+  const int c = (bx << o.lcw) + (tid & ((1 << o.lcw) - 1));
+  if (row >= o.rows || c >= cpr) return;
+  const long q = (long)row * cpr + c;
   const int k0 = c * 8;
   const float *x = o.X + (long)row * o.ld + k0;
   float v[8];
@@ -204,10 +206,16 @@ static SplitOperand split_operand(const float *X, long ld, int rows, bool kcols,
   o.kcols = kcols;
   o.w = reinterpret_cast<u32x4 *>(w);
   o.tiles_c = (rows + kSplitT - 1) / kSplitT;
-  if (kcols)
-    o.blocks = ((long)rows * (Kp / 8) + 255) / 256;
-  else
+  const int cpr = Kp / 8;
+  o.lcw = 0;
+  while ((1 << o.lcw) < cpr && o.lcw < 6) ++o.lcw;
+  o.groups_c = (cpr + (1 << o.lcw) - 1) >> o.lcw;
+  if (kcols) {
+    const int rows_per_group = 256 >> o.lcw;
+    o.blocks = (long)((rows + rows_per_group - 1) / rows_per_group) * o.groups_c;
+  } else {
     o.blocks = (long)o.tiles_c * ((Kp + kSplitT - 1) / kSplitT);
+  }
   vec = (reinterpret_cast<uintptr_t>(X) & 15u) == 0 && ld % 4 == 0 && (kcols || rows % 4 == 0);
   return o;
 }
