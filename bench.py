@@ -320,6 +320,27 @@ def general_table(settle: float) -> list[dict]:
     return rows
 
 
+def shard_table(steps: int, warmup: int, settle: float) -> list[dict]:
+    """One GPU's share of the 8192^3 product when C is split by rows over
+    1, 2, 4 or 8 GPUs (M = 8192 / n, N = K = 8192, B whole): time sgemm_run
+    on that shape.  Measures one GPU only; nothing here runs on several."""
+    import dense_fp32_matrix_03_amd as sg
+    from dense_fp32_matrix_03_amd import inputs
+
+    rows = []
+    for n in (1, 2, 4, 8):
+        M = 8192 // n
+        w = inputs.Workload(f"sgemm_{M}x8192x8192_uniform_seed4", M, 8192, 8192, "uniform", 4,
+                            8192, 8192, 8192, "sampled")
+        ms, finite = time_gpu(w, sg.VARIANTS["mfma"], steps, warmup, warm_seconds=settle)
+        tf = w.flops / (ms * 1e-3) / 1e12
+        r = {"share_of_gpus": n, "workload": w.name, "ms": round(ms, 5), "tflops": round(tf, 2),
+             "pct_of_peak": round(100 * tf / PEAK_TFLOPS, 1), "output_finite": finite}
+        print(json.dumps(r), flush=True)
+        rows.append(r)
+    return rows
+
+
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bfloat16 matrix peak, published
 
@@ -491,6 +512,9 @@ def main(argv=None) -> int:
                     help="time every workload on the GPU and the oracle on the host (1 thread "
                          "and all threads; 8192^3 single-thread extrapolated from the "
                          "2048^3 rate) and print one JSON line per workload")
+    ap.add_argument("--shards", action="store_true",
+                    help="time one GPU's share of 8192^3 split by rows of C over 1, 2, 4 "
+                         "and 8 GPUs (single GPU; one JSON line each)")
     ap.add_argument("--general", action="store_true",
                     help="time the general form (transposes, alpha/beta, strided batches) "
                          "on a fixed set of cases, one JSON line each")
@@ -545,6 +569,10 @@ def main(argv=None) -> int:
         return 0
     if a.vector_add:
         vector_add_table(a.steps, a.settle)
+        sg.sgemm_destroy()
+        return 0
+    if a.shards:
+        shard_table(a.steps, a.warmup, a.settle)
         sg.sgemm_destroy()
         return 0
     if a.general:
