@@ -1,7 +1,10 @@
 // mfma_gemm.hpp -- register-staged matrix-core product (v_mfma_f32_32x32x2_f32).
 //
-// This is the general path: any 4-byte alignment, any leading dimension.
-// Operands that allow it use the buffer-to-LDS kernel of mfma_dma.hpp.
+// sgemm_run uses the buffer-to-LDS kernel of mfma_dma.hpp for every operand
+// whose K slice fits a buffer descriptor (aligned or not); this kernel takes
+// the rest -- a leading dimension so large that one slice spans 2 GiB -- and
+// is the register-staged ablation variant.  Any 4-byte alignment, any
+// leading dimension.
 //
 // Structure (the pages' recipe, re-derived for CDNA4):
 //  * block tiling with a K-sliding window: each work-group owns a BM x BN tile
