@@ -7,7 +7,8 @@
 // used once, so they should not displace other data from the caches, and
 // measured over 2^24 and 2^28 floats this shape beat 2, 4 or 8 chunks per
 // thread, grid-stride loops, 512- and 1024-thread groups and non-temporal
-// stores (6.4 - 6.9 TB/s against 5.7 - 6.1 for plain loads).  If any of A,
+// stores (6.4 - 6.9 TB/s against 5.7 - 6.1 for plain loads, on zero-filled
+// arrays; non-zero data streams about 9% slower).  If any of A,
 // B, C is not 16-byte aligned, a one-float-per-lane kernel (four floats per
 // thread, strided by the group size) runs instead.  Each element is read and
 // written by one thread, loads before the store, so C may be A or B itself.
