@@ -114,6 +114,24 @@ def test_general_edge_sweep(ta, tb):
         assert r.ok, f"{ta}{tb} M={M} N={N} K={K}: {r}"
 
 
+@pytest.mark.parametrize("ta,tb", LAYOUTS, ids=LAYOUT_IDS)
+@pytest.mark.parametrize("pad_a,pad_b", [(0, 3), (1, 0), (4, 8), (5, 7)])
+def test_padded_leading_dimensions(ta, tb, pad_a, pad_b):
+    """Stored operands with NaN-filled columns past their stored width; the
+    widths are multiples of 4, so pads of 0, 4 and 8 keep 16-byte loads and
+    the odd pads force 4-byte ones.  A NaN ever read would reach C."""
+    M, N, K = 132, 96, 76
+    g = np.random.default_rng(149 + 16 * pad_a + pad_b + 2 * int(ta) + int(tb))
+    A, B = _stored(g, ta, tb, M, N, K)
+    A = inputs.padded(A, A.shape[1] + pad_a)
+    B = inputs.padded(B, B.shape[1] + pad_b)
+    C0 = inputs.uniform(g, (M, N))
+    C = _run_ex(ta, tb, M, N, K, 1.25, A, B, -0.5, C0)
+    Cref, Sabs = oracle.sgemm_ex_f64(ta, tb, M, N, K, 1.25, A, B, -0.5, C0)
+    r = oracle.check(C, Cref, Sabs)
+    assert r.ok, f"{ta}{tb} pads {pad_a},{pad_b}: {r}"
+
+
 def test_alpha_zero_and_k_zero_scale_c():
     g = np.random.default_rng(109)
     C0 = inputs.uniform(g, (40, 50))
