@@ -110,6 +110,52 @@ def time_gpu(w, variant: str, steps: int, warmup: int, warm_seconds: float = 0.0
     return per_trial, finite
 
 
+def time_graph(w, variant: str, calls: int = 50, replays: int = 20) -> float:
+    """Per-call GPU time (ms) of `calls` sgemm_run launches captured in one
+    HIP graph and replayed: the kernels run back to back with no host launch
+    cost between them, which is what a short product costs inside a
+    captured sequence."""
+    import torch
+
+    import dense_fp32_matrix_03_amd as sg
+    from dense_fp32_matrix_03_amd import inputs
+
+    A, B = inputs.make_inputs(w)
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(B).cuda()
+    del A, B
+    dC = torch.empty((w.M, w.ldc), dtype=torch.float32, device="cuda")
+
+    def body():
+        for _ in range(calls):
+            sg.sgemm_run_variant(variant, w.M, w.N, w.K, dA, w.lda, dB, w.ldb, dC, w.ldc)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / (calls * replays)
+    del g, dA, dB, dC
+    torch.cuda.empty_cache()
+    return ms
+
+
 def mfma_ceiling(which: int = 0, iters: int = 20000) -> float:
     """TFLOP/s of the library's register-only matrix-core loop (which = 0:
     FP32 32x32x2, 1: bfloat16 32x32x16), best of 5 launches after 2."""
@@ -189,7 +235,9 @@ def workload_table(variant) -> list[dict]:
     """GPU time of sgemm_run (10 trials of R back-to-back calls, R = max(10,
     200 ms / t); median and min) and oracle times, for every workload, with
     the rate as a fraction of the published peak and of the measured
-    matrix-core ceiling."""
+    matrix-core ceiling.  Products under 1e11 flops are also timed inside a
+    captured graph (time_graph), where no host launch cost separates the
+    calls."""
     import statistics
 
     import oracle
@@ -214,6 +262,11 @@ def workload_table(variant) -> list[dict]:
              "pct_of_peak": round(100 * tf / PEAK_TFLOPS, 1),
              "pct_of_mfma_ceiling": round(100 * tf / ceiling, 1), "output_finite": finite,
              "cores": cores}
+        if w.flops < 1e11:
+            # Short products: also the per-call time inside a captured graph.
+            mg = time_graph(w, variant)
+            r.update(gpu_ms_graph=round(mg, 5),
+                     gpu_tflops_graph=round(w.flops / (mg * 1e-3) / 1e12, 2))
         if w.check == "full":
             t1, _ = oracle_seconds(w, 1)
             tn, _ = oracle_seconds(w, cores)

@@ -162,6 +162,9 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
       case SGEMM_VARIANT_MFMA_64:
         err = sgemm::launch_mfma(MfmaTile::T64, MfmaPath::Auto, p, va, vb, s);
         break;
+      case SGEMM_VARIANT_MFMA_32:
+        err = sgemm::launch_mfma(MfmaTile::T32, MfmaPath::Auto, p, va, vb, s);
+        break;
       case SGEMM_VARIANT_MFMA_STAGED:
         err = sgemm::launch_mfma(autotile, MfmaPath::Staged, p, va, vb, s);
         break;
@@ -395,6 +398,7 @@ const char *sgemm_variant_name(int variant) {
     case SGEMM_VARIANT_MFMA_256: return "mfma_256x256";
     case SGEMM_VARIANT_MFMA_128: return "mfma_128x128";
     case SGEMM_VARIANT_MFMA_64: return "mfma_64x64";
+    case SGEMM_VARIANT_MFMA_32: return "mfma_32x32_ksplit4";
     case SGEMM_VARIANT_MFMA_STAGED: return "mfma_register_staged";
     case SGEMM_VARIANT_MFMA_UNPADDED: return "mfma_unpadded_lds";
     default: return nullptr;

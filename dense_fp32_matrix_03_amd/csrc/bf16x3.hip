@@ -534,7 +534,8 @@ hipError_t launch_bf16x3_gemm(MfmaTile tile, const Bf16x3Args &p, hipStream_t st
   switch (tile) {
     case MfmaTile::T256: return launch_bf16x3_cfg<256, 256, 16, 2, 4, 0, 2>(p, stream);
     case MfmaTile::T128: return launch_bf16x3_cfg<128, 128, 32, 2, 4, 1, 2>(p, stream);
-    case MfmaTile::T64: return launch_bf16x3_cfg<64, 64, 32, 2, 2, 1, 2>(p, stream);
+    case MfmaTile::T64:
+    case MfmaTile::T32: return launch_bf16x3_cfg<64, 64, 32, 2, 2, 1, 2>(p, stream);
   }
   return hipErrorInvalidValue;
 }

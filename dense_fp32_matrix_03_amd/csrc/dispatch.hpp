@@ -7,8 +7,10 @@
 
 namespace sgemm {
 
-// Block tiles of the matrix-core kernels.
-enum class MfmaTile { T256, T128, T64 };
+// Block tiles of the matrix-core kernels.  T32 is a 32 x 32 tile whose
+// work-group splits K over four waves (one per SIMD), for products with
+// fewer 64 x 64 tiles than compute units.
+enum class MfmaTile { T256, T128, T64, T32 };
 
 // Which matrix-core kernel:
 //  Auto      buffer-to-LDS loads (16 bytes per lane where va / vb, else
@@ -20,7 +22,7 @@ enum class MfmaTile { T256, T128, T64 };
 enum class MfmaPath { Auto, Staged, Unpadded };
 
 // Largest tile that still gives at least one work-group per compute unit
-// over `batch` products, else the smallest.
+// over `batch` products; T32 when not even 64 x 64 tiles do.
 MfmaTile choose_mfma_tile(long M, long N, int cus, long batch = 1);
 
 // Matrix-core product.  va / vb: A / B qualify for 128-bit loads.

@@ -140,16 +140,26 @@ struct SliceGeom {
 
 // TA / TB: A / B are stored transposed (op(A) = A^T, op(B) = B^T).
 // VA / VB: A / B take 16-byte loads.  KFULL: K % BK == 0.
+// KSPLIT: the work-group runs KSPLIT sets of WM x WN waves over the same
+// tile; set q takes the k groups g with g % KSPLIT == q of every slice, and
+// the sets' partial sums are added in the order 0, 1, .., KSPLIT - 1 through
+// LDS at the end.  A small tile then keeps all four SIMDs of its CU busy,
+// which is what lets a product with fewer 64 x 64 tiles than CUs spread over
+// the whole chip; the order of additions is still fixed for a given call
+// shape.
 template <int BM, int BN, int BK, int WM, int WN, bool SWZ, bool KFULL, int SCHED, bool VA,
-          bool VB, bool TA, bool TB>
-__global__ void __launch_bounds__(WM *WN *kWave)
+          bool VB, bool TA, bool TB, int KSPLIT = 1>
+__global__ void __launch_bounds__(WM *WN *KSPLIT *kWave)
 mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
-  constexpr int NW = WM * WN;
+  constexpr int NWT = WM * WN;       // waves of one k set
+  constexpr int NW = NWT * KSPLIT;   // waves of the work-group
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int KH = BK / 2, G = KH / 4;
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(G >= 2, "BK must be 16 or 32");
+  static_assert(G % KSPLIT == 0, "k groups must split evenly over the k sets");
+  constexpr int GW = G / KSPLIT;  // k groups per slice of one wave
   // A as given has k along its columns; transposed, along its rows.  B the
   // other way round.
   using GA = SliceGeom<BM, BK, TA, VA, SWZ, NW>;
@@ -159,11 +169,17 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   __shared__ __attribute__((aligned(1024))) float As1[BM * BK];
   __shared__ __attribute__((aligned(1024))) float Bs0[BK * BN];
   __shared__ __attribute__((aligned(1024))) float Bs1[BK * BN];
+  // Partial sums of k sets 1 .. KSPLIT-1 for the final reduction.
+  constexpr int kRedSlot = NWT * FM * FN * 16 * kWave;
+  __shared__ __attribute__((aligned(1024))) float Red[KSPLIT > 1 ? (KSPLIT - 1) * kRedSlot : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wm = wave / WN, wn = wave % WN;
+  // k set and wave within the set (KSPLIT == 1: one set, known at compile time)
+  const int kq = KSPLIT > 1 ? wave / NWT : 0;
+  const int wl = KSPLIT > 1 ? wave % NWT : wave;
+  const int wm = wl / WN, wn = wl % WN;
   const int r32 = lane % 32, half = lane / 32;
 
   // Launch position -> (product of the batch, tile).
@@ -236,13 +252,15 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
 
   // Operand read offsets (floats).  In a k-contiguous image, row
   // base + i*32 + r32 (base a multiple of 32) has swizzle kc_swizzle(r32).
+  // Entry i is this wave's i-th k group of a slice, g = kq + KSPLIT * i.
   const int sw = kc_swizzle<BK, SWZ>(r32);
-  int a_off[G], b_off[G];
+  int a_off[GW], b_off[GW];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    a_off[g] = TA ? (half * KH + g * 4) * BM + wm * WTM + r32
+  for (int i = 0; i < GW; ++i) {
+    const int g = kq + KSPLIT * i;
+    a_off[i] = TA ? (half * KH + g * 4) * BM + wm * WTM + r32
                   : (wm * WTM + r32) * BK + 4 * ((half * (KH / 4) + g) ^ sw);
-    b_off[g] = TB ? (wn * WTN + r32) * BK + 4 * ((half * (KH / 4) + g) ^ sw)
+    b_off[i] = TB ? (wn * WTN + r32) * BK + 4 * ((half * (KH / 4) + g) ^ sw)
                   : (half * KH + g * 4) * BN + wn * WTN + r32;
   }
 
@@ -323,8 +341,8 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     constexpr int s = decltype(S)::value;
     using SN = std::integral_constant<int, s ^ 1>;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (g + 1 < G) {
+    for (int g = 0; g < GW; ++g) {
+      if (g + 1 < GW) {
         read_ops(S, g + 1, nxt);
         mma(cur);
         interleave(std::false_type());
@@ -351,6 +369,32 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   // The last slices issued loads past K (zero-filling, no memory traffic);
   // let them retire before the work-group gives up its LDS.
   __builtin_amdgcn_s_waitcnt(0x0f70);
+
+  if constexpr (KSPLIT > 1) {
+    // k sets 1.. leave their sums in LDS; set 0 adds them in order and
+    // stores C.
+    if (kq > 0) {
+      float *red = Red + (kq - 1) * kRedSlot;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            red[(((wl * FM + i) * FN + j) * 16 + e) * kWave + lane] = acc[i][j][e];
+    }
+    __syncthreads();
+    if (kq != 0) return;
+#pragma unroll
+    for (int q = 1; q < KSPLIT; ++q)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            acc[i][j][e] += Red[(q - 1) * kRedSlot + (((wl * FM + i) * FN + j) * 16 + e) * kWave + lane];
+  }
 
   // Epilogue: register e of lane l holds row acc32_row(l, e), column l % 32
   // of its 32x32 block; rows >= M and columns >= N are not stored.  C is read
@@ -391,61 +435,72 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool SWZ, int SCHED, bool VA, bool VB, bool TA,
-          bool TB>
+          bool TB, int KSPLIT>
 inline void launch_dma_kernel(const GemmArgs &p, hipStream_t stream, int group_m) {
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-  const dim3 grid((unsigned)((long)tiles_m * tiles_n * p.batch)), block(WM * WN * kWave);
+  const dim3 grid((unsigned)((long)tiles_m * tiles_n * p.batch)),
+      block(WM * WN * KSPLIT * kWave);
   if (p.K % BK == 0)
     hipLaunchKernelGGL(
-        (mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, true, SCHED, VA, VB, TA, TB>), grid,
-        block, 0, stream, p, tiles_m, tiles_n, group_m);
+        (mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, true, SCHED, VA, VB, TA, TB, KSPLIT>),
+        grid, block, 0, stream, p, tiles_m, tiles_n, group_m);
   else
     hipLaunchKernelGGL(
-        (mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, false, SCHED, VA, VB, TA, TB>), grid,
-        block, 0, stream, p, tiles_m, tiles_n, group_m);
+        (mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, false, SCHED, VA, VB, TA, TB, KSPLIT>),
+        grid, block, 0, stream, p, tiles_m, tiles_n, group_m);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool SWZ, int SCHED, bool TA, bool TB>
+template <int BM, int BN, int BK, int WM, int WN, bool SWZ, int SCHED, bool TA, bool TB,
+          int KSPLIT>
 inline void launch_dma_widths(const GemmArgs &p, bool va, bool vb, hipStream_t stream,
                               int group_m) {
   if (va && vb)
-    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true, TA, TB>(p, stream, group_m);
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true, TA, TB, KSPLIT>(p, stream,
+                                                                                 group_m);
   else if (va)
-    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, false, TA, TB>(p, stream, group_m);
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, false, TA, TB, KSPLIT>(p, stream,
+                                                                                  group_m);
   else if (vb)
-    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, true, TA, TB>(p, stream, group_m);
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, true, TA, TB, KSPLIT>(p, stream,
+                                                                                  group_m);
   else
-    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, false, TA, TB>(p, stream, group_m);
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, false, TA, TB, KSPLIT>(p, stream,
+                                                                                   group_m);
 }
 
 // Plain layout (no transposes).  WIDE_ONLY instantiates only the 16-byte-load
 // form; the caller guarantees va && vb.
 template <int BM, int BN, int BK, int WM, int WN, bool SWZ = true, int SCHED = 1,
-          bool WIDE_ONLY = false>
+          bool WIDE_ONLY = false, int KSPLIT = 1>
 inline hipError_t launch_dma_cfg(const GemmArgs &p, bool va, bool vb, hipStream_t stream,
                                  int group_m = 8) {
   if constexpr (WIDE_ONLY) {
     if (!(va && vb)) return hipErrorInvalidValue;
-    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true, false, false>(p, stream,
-                                                                                group_m);
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true, false, false, KSPLIT>(
+        p, stream, group_m);
   } else {
-    launch_dma_widths<BM, BN, BK, WM, WN, SWZ, SCHED, false, false>(p, va, vb, stream, group_m);
+    launch_dma_widths<BM, BN, BK, WM, WN, SWZ, SCHED, false, false, KSPLIT>(p, va, vb, stream,
+                                                                            group_m);
   }
   return hipGetLastError();
 }
 
 // Any layout.
-template <int BM, int BN, int BK, int WM, int WN>
+template <int BM, int BN, int BK, int WM, int WN, int KSPLIT = 1>
 inline hipError_t launch_dma_general(const GemmArgs &p, bool ta, bool tb, bool va, bool vb,
                                      hipStream_t stream, int group_m = 8) {
   if (!ta && !tb)
-    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, false, false>(p, va, vb, stream, group_m);
+    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, false, false, KSPLIT>(p, va, vb, stream,
+                                                                         group_m);
   else if (!ta)
-    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, false, true>(p, va, vb, stream, group_m);
+    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, false, true, KSPLIT>(p, va, vb, stream,
+                                                                        group_m);
   else if (!tb)
-    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, true, false>(p, va, vb, stream, group_m);
+    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, true, false, KSPLIT>(p, va, vb, stream,
+                                                                        group_m);
   else
-    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, true, true>(p, va, vb, stream, group_m);
+    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, true, true, KSPLIT>(p, va, vb, stream,
+                                                                       group_m);
   return hipGetLastError();
 }
 

@@ -13,6 +13,11 @@ namespace sgemm {
 //   T128  128 x 128 x 32, 4 x 2 waves of  32 x 64  (two waves per SIMD;
 //         the register-staged kernel keeps 2 x 2 waves of 64 x 64)
 //   T64    64 x  64 x 32, 2 x 2 waves of  32 x 32
+//   T32    32 x  32 x 32, 4 waves on the same 32 x 32 block, each taking
+//         one of the four k groups of every slice (KSPLIT = 4); for
+//         products with fewer 64 x 64 tiles than CUs it spreads the work
+//         over four times as many work-groups, each on four SIMDs
+//         (512^3: 10.9 -> 6.7 us; 640 x 640 x 2048: 33.8 -> 26.3 us).
 // At 2048^3 (one 128 x 128 tile per CU) eight waves instead of four took the
 // buffer-to-LDS kernel from 140.7 to 144.9 TFLOP/s; at 4096^3 both give 150.5.
 // WIDE_ONLY: only the 16-byte-load forms are instantiated (the caller
@@ -38,15 +43,16 @@ static hipError_t launch_tile(MfmaPath path, const GemmArgs &p, bool va, bool vb
 
 // The largest tile that still gives every compute unit a work-group and
 // whose tiles are at least 3/4 inside C (a 256 x 256 tile over a 64 x 64
-// product would compute 16 times the useful work); else the smallest.
+// product would compute 16 times the useful work); else 64 x 64 if its
+// tiles fill the compute units, else the k-split 32 x 32 tile.
 MfmaTile choose_mfma_tile(long M, long N, int cus, long batch) {
+  auto tiles = [&](long t) { return (double)((M + t - 1) / t) * ((N + t - 1) / t) * batch; };
   auto good = [&](long t) {
-    const long tm = (M + t - 1) / t, tn = (N + t - 1) / t;
-    return (double)tm * tn * batch >= cus && 4.0 * M * N >= 3.0 * tm * tn * t * t;
+    return tiles(t) >= cus && 4.0 * M * N * batch >= 3.0 * tiles(t) * t * t;
   };
   if (good(256)) return MfmaTile::T256;
   if (good(128)) return MfmaTile::T128;
-  return MfmaTile::T64;
+  return tiles(64) >= cus ? MfmaTile::T64 : MfmaTile::T32;
 }
 
 hipError_t launch_mfma(MfmaTile tile, MfmaPath path, const GemmArgs &p, bool va, bool vb,
@@ -60,15 +66,22 @@ hipError_t launch_mfma(MfmaTile tile, MfmaPath path, const GemmArgs &p, bool va,
     case MfmaTile::T128:
       return launch_tile<128, 128, 32, 2, 2, false, 4, 2>(path, p, va, vb, stream);
     case MfmaTile::T64: return launch_tile<64, 64, 32, 2, 2>(path, p, va, vb, stream);
+    case MfmaTile::T32:
+      // The register-staged kernel has no k split: it takes the 64 x 64 tile.
+      if (path == MfmaPath::Staged || !dma_offsets_fit(32, p.lda, 32, p.ldb))
+        return launch_tile<64, 64, 32, 2, 2>(path, p, va, vb, stream);
+      if (path == MfmaPath::Unpadded)
+        return launch_dma_cfg<32, 32, 32, 1, 1, false, 1, false, 4>(p, va, vb, stream);
+      return launch_dma_cfg<32, 32, 32, 1, 1, true, 1, false, 4>(p, va, vb, stream);
   }
   return hipErrorInvalidValue;
 }
 
-template <int BM, int BN, int BK, int WM, int WN>
+template <int BM, int BN, int BK, int WM, int WN, int KSPLIT = 1>
 static hipError_t launch_general_tile(const GemmArgs &p, bool ta, bool tb, bool va, bool vb,
                                       hipStream_t stream) {
   if (!dma_offsets_fit(ta ? BK : BM, p.lda, tb ? BN : BK, p.ldb)) return hipErrorInvalidValue;
-  return launch_dma_general<BM, BN, BK, WM, WN>(p, ta, tb, va, vb, stream);
+  return launch_dma_general<BM, BN, BK, WM, WN, KSPLIT>(p, ta, tb, va, vb, stream);
 }
 
 hipError_t launch_mfma_general(MfmaTile tile, const GemmArgs &p, bool ta, bool tb, bool va,
@@ -80,6 +93,8 @@ hipError_t launch_mfma_general(MfmaTile tile, const GemmArgs &p, bool ta, bool t
     return launch_dma_cfg<256, 256, 32, 2, 4, true, 1, true>(p, va, vb, stream);
   }
   if (tile == MfmaTile::T64) return launch_general_tile<64, 64, 32, 2, 2>(p, ta, tb, va, vb, stream);
+  if (tile == MfmaTile::T32)
+    return launch_general_tile<32, 32, 32, 1, 1, 4>(p, ta, tb, va, vb, stream);
   return launch_general_tile<128, 128, 32, 4, 2>(p, ta, tb, va, vb, stream);
 }
 

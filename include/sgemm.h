@@ -78,7 +78,10 @@ extern "C" {
  * multiples of 4, else 4 bytes; only an operand whose leading dimension puts
  * one slice beyond 2 GiB is fetched through registers instead.  The
  * _MFMA_<n> variants force its n x n block tile instead of choosing one
- * from the shape.  SGEMM_VARIANT_MFMA_STAGED always fetches through
+ * from the shape; the 32 x 32 tile (which sgemm_run picks when 64 x 64
+ * tiles are fewer than the compute units) runs four waves on the same
+ * block, each summing a quarter of every K slice, and adds their partial
+ * sums in a fixed order.  SGEMM_VARIANT_MFMA_STAGED always fetches through
  * registers, and SGEMM_VARIANT_MFMA_UNPADDED drops the LDS anti-conflict
  * layout (the chapter's padding, section 三): both exist to measure what
  * those steps are worth.
@@ -93,7 +96,8 @@ extern "C" {
 #define SGEMM_VARIANT_MFMA_64 7
 #define SGEMM_VARIANT_MFMA_STAGED 8
 #define SGEMM_VARIANT_MFMA_UNPADDED 9
-#define SGEMM_NUM_VARIANTS 10
+#define SGEMM_VARIANT_MFMA_32 10
+#define SGEMM_NUM_VARIANTS 11
 
 /*
  * Initialise the library for the current device: checks that it is gfx950

@@ -20,7 +20,8 @@ from dense_fp32_matrix_03_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
-MFMA_VARIANTS = ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_staged", "mfma_unpadded"]
+MFMA_VARIANTS = ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_staged", "mfma_unpadded",
+                 "mfma_32"]
 VALU_VARIANTS = ["naive", "lds", "reg", "dbuf"]
 ALL_VARIANTS = VALU_VARIANTS + MFMA_VARIANTS
 
@@ -205,7 +206,7 @@ EXTREME_SHAPES = [(1, 1, 1 << 22), (2, 3, 1 << 20), (1 << 20, 3, 7), (5, 1 << 20
                   (4097, 4099, 1), (1 << 15, 1 << 9, 4)]
 
 
-@pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged"])
+@pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged", "mfma_32"])
 @pytest.mark.parametrize("shape", EXTREME_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_extreme_aspect_ratios(variant, shape):
     M, N, K = shape
@@ -225,7 +226,8 @@ def test_extreme_aspect_ratios(variant, shape):
 DMA_DIMS = [4, 8, 12, 28, 36, 60, 68, 124, 132, 252, 260, 516]
 
 
-@pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_unpadded"])
+@pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_unpadded",
+                                     "mfma_32"])
 def test_buffer_to_lds_edge_sweep(variant):
     g0 = np.random.default_rng(53 + MFMA_VARIANTS.index(variant))
     shapes = [tuple(int(x) for x in g0.choice(DMA_DIMS, 3)) for _ in range(20)]
@@ -258,7 +260,8 @@ def test_load_paths_agree_bitwise(w, tile):
     assert all(o == outs[0] for o in outs[1:])
 
 
-@pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged", "reg", "dbuf"])
+@pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged", "reg", "dbuf",
+                                     "mfma_32"])
 def test_padded_leading_dimensions(variant):
     """NaN in the padding of A and B must not reach C; C's padding is untouched."""
     M, N, K = 200, 136, 72
@@ -291,6 +294,47 @@ def test_misaligned_pointers(variant):
     Cref, Sabs = oracle.sgemm_f64(A, B)
     r = oracle.check(C, Cref, Sabs)
     assert r.ok, str(r)
+
+
+@pytest.mark.parametrize("M,N,K,batch,tile", [
+    (512, 512, 512, 1, "mfma_32"), (256, 256, 256, 1, "mfma_32"), (300, 260, 100, 1, "mfma_32"),
+    (1000, 130, 2048, 1, "mfma_32"), (1024, 1024, 256, 1, "mfma_64"), (64, 64, 64, 256, "mfma_64"),
+    (128, 128, 128, 8, "mfma_32")])
+def test_tile_choice_for_small_products(M, N, K, batch, tile):
+    """Products with fewer 64 x 64 tiles (over the batch) than compute units
+    take the k-split 32 x 32 tile, the others keep 64 x 64: sgemm_run's bits
+    equal those of the forced variant, and both meet the oracle."""
+    import torch
+    g = np.random.default_rng(M + N + K + batch)
+    A = inputs.uniform(g, (batch, M, K))
+    B = inputs.uniform(g, (batch, K, N))
+    dA, dB = _dev(A), _dev(B)
+    outs = []
+    for variant in ("mfma", tile):
+        dC = torch.full((batch, M, N), float("nan"), dtype=torch.float32, device="cuda")
+        if batch == 1:
+            sg.sgemm_run_variant(variant, M, N, K, dA, K, dB, N, dC, N)
+        else:
+            assert variant == "mfma"
+            sg.sgemm_run_strided_batched(0, 0, M, N, K, 1.0, dA, K, M * K, dB, N, K * N, 0.0,
+                                         dC, N, M * N, batch)
+        torch.cuda.synchronize()
+        outs.append(dC.cpu().numpy())
+        if batch > 1:
+            break
+    for b in sorted({0, batch - 1}):
+        Cref, Sabs = oracle.sgemm_f64(A[b], B[b])
+        r = oracle.check(outs[0][b], Cref, Sabs)
+        assert r.ok, f"batch {b}: {r}"
+        assert r.usage < 0.05
+    if batch == 1:
+        assert outs[0].tobytes() == outs[1].tobytes(), f"sgemm_run did not take {tile}"
+    else:
+        # One product of the batch through the forced tile gives the same bits.
+        dC1 = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        sg.sgemm_run_variant(tile, M, N, K, dA[0], K, dB[0], N, dC1, N)
+        torch.cuda.synchronize()
+        assert dC1.cpu().numpy().tobytes() == outs[0][0].tobytes(), f"batch did not take {tile}"
 
 
 def test_identity_gives_A_exactly():
