@@ -8,8 +8,8 @@
 namespace sgemm {
 
 // Block tiles of the matrix-core kernels.  T32 is a 32 x 32 tile whose
-// work-group splits K over four waves (one per SIMD), for products with
-// fewer 64 x 64 tiles than compute units.
+// work-group splits K over four waves (one per SIMD), for products whose
+// 64 x 64 tiles would leave a quarter of the compute units or more idle.
 enum class MfmaTile { T256, T128, T64, T32 };
 
 // Which matrix-core kernel:
@@ -22,7 +22,8 @@ enum class MfmaTile { T256, T128, T64, T32 };
 enum class MfmaPath { Auto, Staged, Unpadded };
 
 // Largest tile that still gives at least one work-group per compute unit
-// over `batch` products; T32 when not even 64 x 64 tiles do.
+// over `batch` products; T32 when 64 x 64 tiles would fill at most 3/4 of
+// the compute units.
 MfmaTile choose_mfma_tile(long M, long N, int cus, long batch = 1);
 
 // Matrix-core product.  va / vb: A / B qualify for 128-bit loads.

@@ -15,9 +15,9 @@ namespace sgemm {
 //   T64    64 x  64 x 32, 2 x 2 waves of  32 x 32
 //   T32    32 x  32 x 32, 4 waves on the same 32 x 32 block, each taking
 //         one of the four k groups of every slice (KSPLIT = 4); for
-//         products with fewer 64 x 64 tiles than CUs it spreads the work
-//         over four times as many work-groups, each on four SIMDs
-//         (512^3: 10.9 -> 6.7 us; 640 x 640 x 2048: 33.8 -> 26.3 us).
+//         products with at most 3/4 as many 64 x 64 tiles as CUs it spreads
+//         the work over four times as many work-groups, each on four SIMDs
+//         (512^3: 11.7 -> 7.3 us; 640 x 640 x 2048: 35.4 -> 26.5 us).
 // At 2048^3 (one 128 x 128 tile per CU) eight waves instead of four took the
 // buffer-to-LDS kernel from 140.7 to 144.9 TFLOP/s; at 4096^3 both give 150.5.
 // WIDE_ONLY: only the 16-byte-load forms are instantiated (the caller
@@ -43,8 +43,12 @@ static hipError_t launch_tile(MfmaPath path, const GemmArgs &p, bool va, bool vb
 
 // The largest tile that still gives every compute unit a work-group and
 // whose tiles are at least 3/4 inside C (a 256 x 256 tile over a 64 x 64
-// product would compute 16 times the useful work); else 64 x 64 if its
-// tiles fill the compute units, else the k-split 32 x 32 tile.
+// product would compute 16 times the useful work); else 64 x 64, unless its
+// tiles would leave more than a quarter of the compute units idle: then the
+// k-split 32 x 32 tile.  (Four 32 x 32 work-groups per 64 x 64 tile; at 3/4
+// of the CUs or fewer they fit in three rounds where 64 x 64 needs one full
+// round each, and the measured crossover lies between 192 and 208 tiles on
+// 256 CUs.)
 MfmaTile choose_mfma_tile(long M, long N, int cus, long batch) {
   auto tiles = [&](long t) { return (double)((M + t - 1) / t) * ((N + t - 1) / t) * batch; };
   auto good = [&](long t) {
@@ -52,7 +56,7 @@ MfmaTile choose_mfma_tile(long M, long N, int cus, long batch) {
   };
   if (good(256)) return MfmaTile::T256;
   if (good(128)) return MfmaTile::T128;
-  return tiles(64) >= cus ? MfmaTile::T64 : MfmaTile::T32;
+  return 4.0 * tiles(64) <= 3.0 * cus ? MfmaTile::T32 : MfmaTile::T64;
 }
 
 hipError_t launch_mfma(MfmaTile tile, MfmaPath path, const GemmArgs &p, bool va, bool vb,

@@ -79,7 +79,7 @@ extern "C" {
  * one slice beyond 2 GiB is fetched through registers instead.  The
  * _MFMA_<n> variants force its n x n block tile instead of choosing one
  * from the shape; the 32 x 32 tile (which sgemm_run picks when 64 x 64
- * tiles are fewer than the compute units) runs four waves on the same
+ * tiles would fill at most 3/4 of the compute units) runs four waves on the same
  * block, each summing a quarter of every K slice, and adds their partial
  * sums in a fixed order.  SGEMM_VARIANT_MFMA_STAGED always fetches through
  * registers, and SGEMM_VARIANT_MFMA_UNPADDED drops the LDS anti-conflict

@@ -299,11 +299,12 @@ def test_misaligned_pointers(variant):
 @pytest.mark.parametrize("M,N,K,batch,tile", [
     (512, 512, 512, 1, "mfma_32"), (256, 256, 256, 1, "mfma_32"), (300, 260, 100, 1, "mfma_32"),
     (1000, 130, 2048, 1, "mfma_32"), (1024, 1024, 256, 1, "mfma_64"), (64, 64, 64, 256, "mfma_64"),
-    (128, 128, 128, 8, "mfma_32")])
+    (128, 128, 128, 8, "mfma_32"), (768, 1024, 512, 1, "mfma_32"), (832, 1024, 512, 1, "mfma_64")])
 def test_tile_choice_for_small_products(M, N, K, batch, tile):
-    """Products with fewer 64 x 64 tiles (over the batch) than compute units
-    take the k-split 32 x 32 tile, the others keep 64 x 64: sgemm_run's bits
-    equal those of the forced variant, and both meet the oracle."""
+    """Products whose 64 x 64 tiles (over the batch) would fill at most 3/4
+    of the 256 compute units take the k-split 32 x 32 tile (768 x 1024: 192
+    tiles), the others keep 64 x 64 (832 x 1024: 208): sgemm_run's bits equal
+    those of the forced variant, and both meet the oracle."""
     import torch
     g = np.random.default_rng(M + N + K + batch)
     A = inputs.uniform(g, (batch, M, K))
