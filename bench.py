@@ -2,6 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--variant V] [--no-cpu-baseline] [--no-secondary]
+    python bench.py --table | --general | --shards | --ladder | --vector-add
+                    | --bf16x3 | --bf16x3-general | --copy-calibration
 
 One step is one call of sgemm_run on the 8192^3 workload (uniform[-1, 1)
 inputs from seed 4, already resident in HBM).  W untimed calls, then exactly
@@ -9,6 +11,13 @@ K calls between two synchronisations, timed with HIP events recorded on the
 stream the kernels run on.  Prints one JSON line.  The 2048^3 workload is
 timed the same way (200 calls, after 0.3 s of untimed calls so that the
 clocks have settled) and reported under "secondary".
+
+The other modes print one JSON line per case: every workload with oracle
+times (--table), the general form and strided batches (--general), one
+GPU's share of 8192^3 split by rows over 1-8 GPUs (--shards), the pages'
+progression (--ladder), the vector add (--vector-add), the bfloat16 split
+path (--bf16x3, --bf16x3-general), and the copy that calibrates the HBM
+counters (--copy-calibration).
 
 The CPU baseline is the oracle (double-precision triple loop) timed on the
 host cores on a bounded sample of the same workload: the first R rows of C,
