@@ -119,6 +119,9 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
   int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc);
   if (rc != SGEMM_OK) return rc;
   if (variant <= SGEMM_VARIANT_DBUF && !grid_fits(M, N, 1, 16, 256)) return SGEMM_ERR_TOO_LARGE;
+  // The forced 32 x 32 tile runs 256 threads per 32 x 32 block (sgemm_run
+  // only picks it for products far below this limit).
+  if (variant == SGEMM_VARIANT_MFMA_32 && !grid_fits(M, N, 1, 32, 256)) return SGEMM_ERR_TOO_LARGE;
   if (!g_ready.load(std::memory_order_acquire)) return SGEMM_ERR_NOT_INITIALIZED;
   if (M == 0 || N == 0) return SGEMM_OK;
   DeviceInfo di;

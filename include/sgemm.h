@@ -43,7 +43,8 @@
  * even before sgemm_create.  sgemm_status_string() names each status.
  * Limits (SGEMM_ERR_TOO_LARGE): M, N, K and batch below 2^31, and one launch
  * below 2^32 work-items -- 256 per 64 x 64 block of C for the matrix-core
- * kernels, 256 per 16 x 16 block for the vector-FMA variants.
+ * kernels (per 32 x 32 block for SGEMM_VARIANT_MFMA_32), 256 per 16 x 16
+ * block for the vector-FMA variants.
  *
  * Threads.  sgemm_create / sgemm_destroy are serialised internally;
  * sgemm_run may be called from any thread once sgemm_create has succeeded.

@@ -81,6 +81,20 @@ def test_unknown_variant_rejected():
     assert sg.sgemm_status_string(rc) == "SGEMM_ERR_INVALID_VALUE"
 
 
+def test_forced_tile_work_item_limits():
+    """A launch must stay below 2^32 work-items: 131072 x 131072 fits with
+    64 x 64 blocks (2^22 blocks x 256) but not with the forced 32 x 32 tile
+    (2^24 x 256); the checks come before anything touches the runtime."""
+    lib = sg.load_library()
+    n = 131072
+    rc = lib.sgemm_run_variant(sg.VARIANTS["mfma_32"], n, n, 1, 16, 1, 16, n, 16, n, None)
+    assert sg.sgemm_status_string(rc) == "SGEMM_ERR_TOO_LARGE"
+    rc = lib.sgemm_run_variant(sg.VARIANTS["mfma_64"], n, n, 1, 16, 1, 16, n, 16, n, None)
+    assert sg.sgemm_status_string(rc) == "SGEMM_ERR_NOT_INITIALIZED"
+    rc = lib.sgemm_run_variant(sg.VARIANTS["dbuf"], n, n, 1, 16, 1, 16, n, 16, n, None)
+    assert sg.sgemm_status_string(rc) == "SGEMM_ERR_TOO_LARGE"
+
+
 def test_destroy_without_create():
     lib = sg.load_library()
     assert sg.sgemm_status_string(lib.sgemm_destroy()) == "SGEMM_ERR_NOT_INITIALIZED"
