@@ -2,8 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--variant V] [--no-cpu-baseline] [--no-secondary]
-    python bench.py --table | --general | --shards | --ladder | --vector-add
-                    | --bf16x3 | --bf16x3-general | --copy-calibration
+    python bench.py --table | --general | --small | --shards | --ladder
+                    | --vector-add | --bf16x3 | --bf16x3-general | --copy-calibration
 
 One step is one call of sgemm_run on the 8192^3 workload (uniform[-1, 1)
 inputs from seed 4, already resident in HBM).  W untimed calls, then exactly
@@ -13,7 +13,8 @@ timed the same way (200 calls, after 0.3 s of untimed calls so that the
 clocks have settled) and reported under "secondary".
 
 The other modes print one JSON line per case: every workload with oracle
-times (--table), the general form and strided batches (--general), one
+times (--table), the general form and strided batches (--general), small
+products with and without the k-split 32 x 32 tile (--small), one
 GPU's share of 8192^3 split by rows over 1-8 GPUs (--shards), the pages'
 progression (--ladder), the vector add (--vector-add), the bfloat16 split
 path (--bf16x3, --bf16x3-general), and the copy that calibrates the HBM
@@ -382,6 +383,57 @@ def general_table(settle: float) -> list[dict]:
     return rows
 
 
+# Products with few 64 x 64 tiles: (M, N, K).  The last two sit on either
+# side of the point where sgemm_run switches to the k-split 32 x 32 tile.
+SMALL = ((256, 256, 256), (300, 260, 100), (512, 512, 512), (768, 768, 768),
+         (640, 640, 2048), (1000, 130, 2048), (768, 1024, 512), (832, 1024, 512))
+
+
+def small_table(steps: int) -> list[dict]:
+    """sgemm_run on the SMALL shapes with the 64 x 64 tile forced, then with
+    the tile sgemm_run chooses; HIP-event time per call over `steps` calls
+    (which for the shortest includes the host's launch cost; a kernel trace
+    gives the kernels' own durations)."""
+    import numpy as np
+    import torch
+
+    import dense_fp32_matrix_03_amd as sg
+    from dense_fp32_matrix_03_amd import inputs
+
+    rows = []
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    for M, N, K in SMALL:
+        g = np.random.default_rng(M + N + K)
+        dA = torch.from_numpy(inputs.uniform(g, (M, K))).cuda()
+        dB = torch.from_numpy(inputs.uniform(g, (K, N))).cuda()
+        dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        for variant in ("mfma_64", "mfma"):
+            def step():
+                sg.sgemm_run_variant(variant, M, N, K, dA, K, dB, N, dC, N, h)
+
+            for _ in range(10):
+                step()
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            for _ in range(steps):
+                step()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1) / steps
+            r = {"M": M, "N": N, "K": K, "variant": sg.sgemm_variant_name(sg.VARIANTS[variant]),
+                 "calls": 10 + steps, "us": round(ms * 1e3, 2),
+                 "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2),
+                 "output_finite": bool(torch.isfinite(dC).all().item())}
+            print(json.dumps(r), flush=True)
+            rows.append(r)
+        del dA, dB, dC
+    torch.cuda.empty_cache()
+    return rows
+
+
 def shard_table(steps: int, warmup: int, settle: float) -> list[dict]:
     """One GPU's share of the 8192^3 product when C is split by rows over
     1, 2, 4 or 8 GPUs (M = 8192 / n, N = K = 8192, B whole): time sgemm_run
@@ -574,6 +626,9 @@ def main(argv=None) -> int:
                     help="time every workload on the GPU and the oracle on the host (1 thread "
                          "and all threads; 8192^3 single-thread extrapolated from the "
                          "2048^3 rate) and print one JSON line per workload")
+    ap.add_argument("--small", action="store_true",
+                    help="time products with few 64x64 tiles with the 64x64 tile forced and "
+                         "with the tile sgemm_run picks (one JSON line each)")
     ap.add_argument("--shards", action="store_true",
                     help="time one GPU's share of 8192^3 split by rows of C over 1, 2, 4 "
                          "and 8 GPUs (single GPU; one JSON line each)")
@@ -631,6 +686,10 @@ def main(argv=None) -> int:
         return 0
     if a.vector_add:
         vector_add_table(a.steps, a.settle)
+        sg.sgemm_destroy()
+        return 0
+    if a.small:
+        small_table(max(a.steps, 100))
         sg.sgemm_destroy()
         return 0
     if a.shards:
