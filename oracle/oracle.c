@@ -240,8 +240,8 @@ int oracle_vector_add(int64_t n, const float *A, const float *B, float *C)
  * its performance table) but gives no method; the reading taken here is the
  * usual one for carrying single precision through low-precision matrix
  * cores: split each operand into pieces the cores take exactly.  bfloat16
- * keeps the float exponent and 8 significant bits.  Each piece is the value with 8 significant bits nearest
- * to what is left, ties to even:
+ * keeps the float exponent and 8 significant bits.  Each piece is the value
+ * with 8 significant bits nearest to what is left, ties to even:
  *   x0 = rn8(x),  x1 = rn8(x - x0),  x2 = rn8(x - x0 - x1).
  * rn8 is written from its definition: x = f * 2^e with 1/2 <= |f| < 1, and
  * the result is nearbyint(f * 2^8) * 2^(e - 8) (nearbyint rounds to nearest
