@@ -17,7 +17,7 @@ from dense_fp32_matrix_03_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
-CASES = 120
+CASES = 400
 
 
 @pytest.fixture(scope="module", autouse=True)
