@@ -354,6 +354,27 @@ def test_deterministic_bits():
     assert C1.tobytes() == C2.tobytes()
 
 
+@pytest.mark.parametrize("M,N,K", [(512, 512, 512), (300, 260, 777), (1000, 130, 2048)])
+def test_deterministic_bits_k_split_tile(M, N, K):
+    """The k-split 32 x 32 tile adds its four partial sums in a fixed order:
+    repeated calls, on two streams, give identical bits."""
+    import torch
+    g = np.random.default_rng(M + N + K)
+    A = inputs.normal(g, (M, K))
+    B = inputs.normal(g, (K, N))
+    dA, dB = _dev(A), _dev(B)
+    outs = []
+    for _ in range(2):
+        for s in (torch.cuda.current_stream(), torch.cuda.Stream()):
+            dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+            s.wait_stream(torch.cuda.current_stream())  # the fill above comes first
+            sg.sgemm_run(M, N, K, dA, K, dB, N, dC, N, s)
+            s.synchronize()
+            outs.append(dC.cpu().numpy().tobytes())
+    assert all(o == outs[0] for o in outs[1:])
+    assert not np.isnan(np.frombuffer(outs[0], dtype=np.float32)).any()
+
+
 # -- degenerate sizes and errors --------------------------------------------------------
 
 def test_k_zero_writes_zeros():
