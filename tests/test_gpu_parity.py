@@ -296,16 +296,20 @@ def test_misaligned_pointers(variant):
     assert r.ok, str(r)
 
 
-@pytest.mark.parametrize("M,N,K,batch,tile", [
-    (512, 512, 512, 1, "mfma_32"), (256, 256, 256, 1, "mfma_32"), (300, 260, 100, 1, "mfma_32"),
-    (1000, 130, 2048, 1, "mfma_32"), (1024, 1024, 256, 1, "mfma_64"), (64, 64, 64, 256, "mfma_64"),
-    (128, 128, 128, 8, "mfma_32"), (768, 1024, 512, 1, "mfma_32"), (832, 1024, 512, 1, "mfma_64")])
-def test_tile_choice_for_small_products(M, N, K, batch, tile):
+@pytest.mark.parametrize("M,N,K,batch", [
+    (512, 512, 512, 1), (256, 256, 256, 1), (300, 260, 100, 1), (1000, 130, 2048, 1),
+    (1024, 1024, 256, 1), (64, 64, 64, 256), (128, 128, 128, 8), (768, 1024, 512, 1),
+    (832, 1024, 512, 1)])
+def test_tile_choice_for_small_products(M, N, K, batch):
     """Products whose 64 x 64 tiles (over the batch) would fill at most 3/4
-    of the 256 compute units take the k-split 32 x 32 tile (768 x 1024: 192
-    tiles), the others keep 64 x 64 (832 x 1024: 208): sgemm_run's bits equal
-    those of the forced variant, and both meet the oracle."""
+    of the compute units take the k-split 32 x 32 tile (on 256 CUs: 768 x
+    1024 with 192 tiles), the others keep 64 x 64 (832 x 1024: 208 tiles):
+    sgemm_run's bits equal those of the forced variant, and both meet the
+    oracle."""
     import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles64 = ((M + 63) // 64) * ((N + 63) // 64) * batch
+    tile = "mfma_32" if 4 * tiles64 <= 3 * cus else "mfma_64"
     g = np.random.default_rng(M + N + K + batch)
     A = inputs.uniform(g, (batch, M, K))
     B = inputs.uniform(g, (batch, K, N))
