@@ -74,6 +74,19 @@ def measured_traffic(workload: str):
     return c.get("hbm_bytes_per_launch")
 
 
+# Library calls made by this process, in order, and the range of them that
+# the last time_gpu() timed: (index of its first timed call, number of timed
+# calls).  Each sgemm_run launches one kernel, so with --trace-summary these
+# index the library's dispatches in a rocprofv3 kernel trace of the run.
+_CALLS = [0]
+LAST_TIMED = [(0, 0)]
+
+
+def trace_fields() -> dict:
+    first, n = LAST_TIMED[0]
+    return {"trace_first": first, "trace_calls": n}
+
+
 def time_gpu(w, variant: str, steps: int, warmup: int, warm_seconds: float = 0.0,
              trials: int = 1):
     import torch
@@ -91,6 +104,7 @@ def time_gpu(w, variant: str, steps: int, warmup: int, warm_seconds: float = 0.0
 
     def step():
         sg.sgemm_run_variant(variant, w.M, w.N, w.K, dA, w.lda, dB, w.ldb, dC, w.ldc, h)
+        _CALLS[0] += 1
 
     for _ in range(warmup):
         step()
@@ -103,6 +117,7 @@ def time_gpu(w, variant: str, steps: int, warmup: int, warm_seconds: float = 0.0
             step()
         torch.cuda.synchronize()
     per_trial = []
+    LAST_TIMED[0] = (_CALLS[0], steps * trials)
     for _ in range(trials):
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
@@ -291,7 +306,7 @@ def workload_table(variant) -> list[dict]:
     return rows
 
 
-LADDER = ("naive", "lds", "reg", "dbuf", "mfma_unpadded", "mfma_staged", "mfma")
+LADDER = ("naive", "lds", "reg", "dbuf", "mfma_unpadded", "mfma_staged", "mfma_dword", "mfma")
 
 
 def ladder(w, steps: int, warmup: int, settle: float) -> list[dict]:
@@ -303,11 +318,13 @@ def ladder(w, steps: int, warmup: int, settle: float) -> list[dict]:
         v = sg.VARIANTS[name]
         ms, finite = time_gpu(w, v, steps, warmup, warm_seconds=settle)
         tf = w.flops / (ms * 1e-3) / 1e12
-        r = {"workload": w.name, "variant": sg.sgemm_variant_name(v), "ms": round(ms, 5),
+        r = {"case": sg.sgemm_variant_name(v), "workload": w.name, "M": w.M, "N": w.N,
+             "K": w.K, "variant": sg.sgemm_variant_name(v), "ms": round(ms, 5),
              "tflops": round(tf, 3), "pct_of_peak": round(100 * tf / PEAK_TFLOPS, 2),
-             "output_finite": finite}
+             "output_finite": finite, **trace_fields()}
         print(json.dumps(r), flush=True)
         rows.append(r)
+    print(json.dumps({"trace_total_calls": _CALLS[0]}), flush=True)
     return rows
 
 
@@ -432,6 +449,116 @@ def small_table(steps: int) -> list[dict]:
         del dA, dB, dC
     torch.cuda.empty_cache()
     return rows
+
+
+# Fixed cost and per-k cost of one launch: M = N in KSCAN_MN, K in KSCAN_K
+# (t = a + b K per shape), after two floor cases, then the five workloads.
+KSCAN_MN = (256, 1024)
+KSCAN_K = (32, 64, 128, 256, 512, 1024, 2048, 4096)
+
+
+def kscan_cases():
+    """(label, Workload) in the order --kscan runs them."""
+    from dense_fp32_matrix_03_amd import inputs
+
+    def w(M, N, K, seed=11):
+        return inputs.Workload(f"sgemm_{M}x{N}x{K}_uniform_seed{seed}", M, N, K, "uniform",
+                               seed, max(K, 1), N, N, "full")
+
+    cases = [("floor: K = 0 (zero fill, no operand read)", w(256, 256, 0)),
+             ("floor: one 32x32 tile", w(32, 32, 32))]
+    for mn in KSCAN_MN:
+        for k in KSCAN_K:
+            cases.append((f"kscan M=N={mn}", w(mn, mn, k)))
+    for wl in inputs.WORKLOADS:
+        cases.append(("workload", wl))
+    return cases
+
+
+def kscan_table(variant, calls: int) -> list[dict]:
+    """HIP-event time per call of sgemm_run on every kscan case (`calls`
+    back-to-back calls after 20 untimed ones and 0.1 s of settling; 20 calls
+    for 8192^3), one JSON line each with the range of library dispatches it
+    timed (trace_first, trace_calls) for --trace-summary."""
+    rows = []
+    for label, w in kscan_cases():
+        n = calls if w.flops < 1e12 else 20
+        ms, finite = time_gpu(w, variant, n, 20 if n == calls else 3, warm_seconds=0.1)
+        r = {"case": label, "workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+             "us": round(ms * 1e3, 3),
+             "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2) if w.K else 0.0,
+             "output_finite": finite, **trace_fields()}
+        print(json.dumps(r), flush=True)
+        rows.append(r)
+    print(json.dumps({"trace_total_calls": _CALLS[0]}), flush=True)
+    return rows
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def trace_summary(trace_csv: str, cases_jsonl: str, counters_csv: str | None = None) -> str:
+    """Markdown table of kernel-trace durations (and, given a counter CSV of
+    the same command, per-dispatch counter means) for every case line of a
+    bench run's output that carries trace_first / trace_calls.  The
+    library's dispatches are those whose kernel lives in namespace sgemm::,
+    taken in dispatch order; their count must equal the run's
+    trace_total_calls.  Runs on the host, no GPU."""
+    import statistics
+
+    cases, total = [], None
+    with open(cases_jsonl) as f:
+        for line in f:
+            line = line.strip()
+            if not line.startswith("{"):
+                continue
+            d = json.loads(line)
+            if "trace_total_calls" in d:
+                total = d["trace_total_calls"]
+            elif "trace_first" in d:
+                cases.append(d)
+
+    def ours(name):
+        return "sgemm::" in name
+
+    disp = sorted((r for r in _read_csv(trace_csv) if ours(r["Kernel_Name"])),
+                  key=lambda r: int(r["Dispatch_Id"]))
+    if total is not None and len(disp) != total:
+        raise ValueError(f"{len(disp)} library dispatches in the trace, run made {total} calls")
+    counters = {}
+    if counters_csv:
+        per = {}
+        for r in _read_csv(counters_csv):
+            if ours(r["Kernel_Name"]):
+                per.setdefault(int(r["Dispatch_Id"]), {})[r["Counter_Name"]] = \
+                    float(r["Counter_Value"])
+        order = sorted(per)
+        if total is not None and len(order) != total:
+            raise ValueError(f"{len(order)} library dispatches in the counters, run made "
+                             f"{total} calls")
+        counters = {i: per[d] for i, d in enumerate(order)}
+    names = sorted({k for v in counters.values() for k in v})
+    head = ["case", "M x N x K", "kernel", "dispatches", "mean us", "median us", "min us",
+            "TFLOP/s (mean)"] + names
+    out = ["| " + " | ".join(head) + " |", "|" + "---|" * len(head)]
+    for c in cases:
+        i0, n = c["trace_first"], c["trace_calls"]
+        rows = disp[i0:i0 + n]
+        us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3 for r in rows]
+        kern = rows[0]["Kernel_Name"].split("(")[0].replace("void ", "").replace("sgemm::", "")
+        mean = statistics.mean(us)
+        fl = 2.0 * c["M"] * c["N"] * c["K"]
+        cells = [c.get("case", ""), f'{c["M"]}x{c["N"]}x{c["K"]}', f"`{kern}`", str(n),
+                 f"{mean:.3f}", f"{statistics.median(us):.3f}", f"{min(us):.3f}",
+                 f"{fl / (mean * 1e-6) / 1e12:.2f}" if fl else "-"]
+        for k in names:
+            vals = [counters[i][k] for i in range(i0, i0 + n) if k in counters.get(i, {})]
+            cells.append(f"{statistics.mean(vals):.4g}" if vals else "-")
+        out.append("| " + " | ".join(cells) + " |")
+    return "\n".join(out)
 
 
 def shard_table(steps: int, warmup: int, settle: float) -> list[dict]:
@@ -644,10 +771,24 @@ def main(argv=None) -> int:
     ap.add_argument("--bf16x3-general", action="store_true",
                     help="time sgemm_run_bf16x3_ex (stored transposes; alpha/beta) at "
                          "2048^3 and 8192^3, one JSON line each")
+    ap.add_argument("--kscan", action="store_true",
+                    help="time sgemm_run at M = N = 256 and 1024 over K = 32 .. 4096, two "
+                         "floor cases and the five workloads, one JSON line each (with the "
+                         "dispatch range each case timed, for --trace-summary)")
+    ap.add_argument("--trace-summary", nargs="+", metavar=("TRACE_CSV", "CASES_JSONL"),
+                    help="host only: summarise a rocprofv3 kernel trace (and optionally a "
+                         "counter CSV) of a bench run per case: TRACE_CSV CASES_JSONL "
+                         "[COUNTERS_CSV]")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     a = ap.parse_args(argv)
+
+    if a.trace_summary:
+        if len(a.trace_summary) not in (2, 3):
+            ap.error("--trace-summary takes TRACE_CSV CASES_JSONL [COUNTERS_CSV]")
+        print(trace_summary(*a.trace_summary))
+        return 0
 
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
@@ -686,6 +827,10 @@ def main(argv=None) -> int:
         return 0
     if a.vector_add:
         vector_add_table(a.steps, a.settle)
+        sg.sgemm_destroy()
+        return 0
+    if a.kscan:
+        kscan_table(variant, max(a.steps, 200))
         sg.sgemm_destroy()
         return 0
     if a.small:

@@ -174,6 +174,10 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
       case SGEMM_VARIANT_MFMA_UNPADDED:
         err = sgemm::launch_mfma(autotile, MfmaPath::Unpadded, p, va, vb, s);
         break;
+      case SGEMM_VARIANT_MFMA_DWORD:
+        // 4-byte loads for both operands whatever their alignment.
+        err = sgemm::launch_mfma(autotile, MfmaPath::Auto, p, false, false, s);
+        break;
       default:
         err = sgemm::launch_mfma(autotile, MfmaPath::Auto, p, va, vb, s);
         break;
@@ -404,6 +408,7 @@ const char *sgemm_variant_name(int variant) {
     case SGEMM_VARIANT_MFMA_32: return "mfma_32x32_ksplit4";
     case SGEMM_VARIANT_MFMA_STAGED: return "mfma_register_staged";
     case SGEMM_VARIANT_MFMA_UNPADDED: return "mfma_unpadded_lds";
+    case SGEMM_VARIANT_MFMA_DWORD: return "mfma_dword_loads";
     default: return nullptr;
   }
 }

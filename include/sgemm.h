@@ -83,9 +83,12 @@ extern "C" {
  * tiles would fill at most 3/4 of the compute units) runs four waves on the same
  * block, each summing a quarter of every K slice, and adds their partial
  * sums in a fixed order.  SGEMM_VARIANT_MFMA_STAGED always fetches through
- * registers, and SGEMM_VARIANT_MFMA_UNPADDED drops the LDS anti-conflict
- * layout (the chapter's padding, section 三): both exist to measure what
- * those steps are worth.
+ * registers, SGEMM_VARIANT_MFMA_UNPADDED drops the LDS anti-conflict
+ * layout (the chapter's padding, section 三), and SGEMM_VARIANT_MFMA_DWORD
+ * fetches both operands 4 bytes per lane even where 16-byte loads are
+ * allowed (the article's coalescing section, "内存合并访问原理": the width
+ * of each lane's access sets how many bytes one wave instruction moves):
+ * all three exist to measure what those steps are worth.
  */
 #define SGEMM_VARIANT_NAIVE 0
 #define SGEMM_VARIANT_LDS 1
@@ -98,7 +101,8 @@ extern "C" {
 #define SGEMM_VARIANT_MFMA_STAGED 8
 #define SGEMM_VARIANT_MFMA_UNPADDED 9
 #define SGEMM_VARIANT_MFMA_32 10
-#define SGEMM_NUM_VARIANTS 11
+#define SGEMM_VARIANT_MFMA_DWORD 11
+#define SGEMM_NUM_VARIANTS 12
 
 /*
  * Initialise the library for the current device: checks that it is gfx950

@@ -21,7 +21,7 @@ from dense_fp32_matrix_03_amd import inputs
 pytestmark = pytest.mark.gpu
 
 MFMA_VARIANTS = ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_staged", "mfma_unpadded",
-                 "mfma_32"]
+                 "mfma_32", "mfma_dword"]
 VALU_VARIANTS = ["naive", "lds", "reg", "dbuf"]
 ALL_VARIANTS = VALU_VARIANTS + MFMA_VARIANTS
 
@@ -38,17 +38,48 @@ def _dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
+# C sits inside a NaN-filled buffer: GUARD_LEAD floats before its first
+# element (an odd count, so C's base is 4-byte but not 16-byte aligned) and
+# GUARD_ROWS rows of ldc floats after its last row.  A store outside the M x N
+# block (rows >= M, columns in [N, ldc), or before the base) shows up as a
+# guard or padding value that is no longer NaN.  Out-of-range positions must
+# not be touched: textbook chapter "4. 矩阵乘法性能优化", section 三
+# (boundary handling).
+GUARD_LEAD = 37
+GUARD_ROWS = 3
+
+
 def _run(A, B, M, N, K, variant="mfma", ldc=None, lda=None, ldb=None):
-    """Run one product on the GPU from host arrays; return C (M x ldc) on the host."""
+    """Run one product on the GPU from host arrays; return C (M x ldc) on the
+    host after checking that every float around the M x N block is still NaN."""
     import torch
     lda = A.shape[1] if lda is None else lda
     ldb = B.shape[1] if ldb is None else ldb
     ldc = max(N, 1) if ldc is None else ldc
     dA, dB = _dev(A), _dev(B)
-    dC = torch.full((max(M, 1), ldc), float("nan"), dtype=torch.float32, device="cuda")
-    sg.sgemm_run_variant(variant, M, N, K, dA, lda, dB, ldb, dC, ldc)
+    rows = max(M, 1)
+    buf = torch.full((GUARD_LEAD + (rows + GUARD_ROWS) * ldc,), float("nan"),
+                     dtype=torch.float32, device="cuda")
+    sg.sgemm_run_variant(variant, M, N, K, dA, lda, dB, ldb, buf.data_ptr() + 4 * GUARD_LEAD,
+                         ldc)
     torch.cuda.synchronize()
-    return dC.cpu().numpy()[:M]
+    host = buf.cpu().numpy()
+    _check_guards(host, M, N, ldc)
+    return host[GUARD_LEAD:GUARD_LEAD + rows * ldc].reshape(rows, ldc)[:M]
+
+
+def _check_guards(host, M, N, ldc):
+    """Every float of `host` outside the M x N block that starts GUARD_LEAD
+    floats in (row stride ldc) is NaN."""
+    assert np.all(np.isnan(host[:GUARD_LEAD])), "a store landed before C's first element"
+    rows = max(M, 1)
+    tail = host[GUARD_LEAD + rows * ldc:]
+    assert tail.size == GUARD_ROWS * ldc
+    assert np.all(np.isnan(tail)), "a store landed after C's last row"
+    body = host[GUARD_LEAD:GUARD_LEAD + rows * ldc].reshape(rows, ldc)
+    assert np.all(np.isnan(body[:, N:])), "a store landed in C's padding columns"
+    if M == 0:
+        assert np.all(np.isnan(body)), "a product with M = 0 wrote C"
 
 
 # -- layout probe ---------------------------------------------------------------
@@ -227,7 +258,7 @@ DMA_DIMS = [4, 8, 12, 28, 36, 60, 68, 124, 132, 252, 260, 516]
 
 
 @pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_unpadded",
-                                     "mfma_32"])
+                                     "mfma_32", "mfma_dword"])
 def test_buffer_to_lds_edge_sweep(variant):
     g0 = np.random.default_rng(53 + MFMA_VARIANTS.index(variant))
     shapes = [tuple(int(x) for x in g0.choice(DMA_DIMS, 3)) for _ in range(20)]
@@ -246,13 +277,13 @@ def test_buffer_to_lds_edge_sweep(variant):
                          ids=["1024", "2048"])
 def test_load_paths_agree_bitwise(w, tile):
     """Buffer-to-LDS and register-staged fetches, with or without the LDS
-    anti-conflict layout, feed the same matrix-core sequence: at the tile
-    the shape selects they must give identical bits."""
+    anti-conflict layout, 16 or 4 bytes per lane, feed the same matrix-core
+    sequence: at the tile the shape selects they must give identical bits."""
     import torch
     A, B = inputs.make_inputs(w)
     dA, dB = _dev(A), _dev(B)
     outs = []
-    for variant in ("mfma", tile, "mfma_staged", "mfma_unpadded"):
+    for variant in ("mfma", tile, "mfma_staged", "mfma_unpadded", "mfma_dword"):
         dC = torch.full((w.M, w.N), float("nan"), dtype=torch.float32, device="cuda")
         sg.sgemm_run_variant(variant, w.M, w.N, w.K, dA, w.K, dB, w.N, dC, w.N)
         torch.cuda.synchronize()
@@ -261,7 +292,7 @@ def test_load_paths_agree_bitwise(w, tile):
 
 
 @pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged", "reg", "dbuf",
-                                     "mfma_32"])
+                                     "mfma_32", "mfma_dword"])
 def test_padded_leading_dimensions(variant):
     """NaN in the padding of A and B must not reach C; C's padding is untouched."""
     M, N, K = 200, 136, 72
@@ -286,11 +317,14 @@ def test_misaligned_pointers(variant):
     B = inputs.uniform(g, (K, N))
     bufA = _dev(np.concatenate([np.zeros(1, np.float32), A.ravel()]))
     bufB = _dev(np.concatenate([np.zeros(3, np.float32), B.ravel()]))
-    dC = torch.full((M * N + 1,), float("nan"), dtype=torch.float32, device="cuda")
+    dC = torch.full((GUARD_LEAD + (M + GUARD_ROWS) * N,), float("nan"), dtype=torch.float32,
+                    device="cuda")
     sg.sgemm_run_variant(variant, M, N, K, bufA.data_ptr() + 4, K, bufB.data_ptr() + 12, N,
-                         dC.data_ptr() + 4, N)
+                         dC.data_ptr() + 4 * GUARD_LEAD, N)
     torch.cuda.synchronize()
-    C = dC.cpu().numpy()[1:].reshape(M, N)
+    host = dC.cpu().numpy()
+    _check_guards(host, M, N, N)
+    C = host[GUARD_LEAD:GUARD_LEAD + M * N].reshape(M, N)
     Cref, Sabs = oracle.sgemm_f64(A, B)
     r = oracle.check(C, Cref, Sabs)
     assert r.ok, str(r)
