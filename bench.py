@@ -506,7 +506,8 @@ def trace_summary(trace_csv: str, cases_jsonl: str, counters_csv: str | None = N
     bench run's output that carries trace_first / trace_calls.  The
     library's dispatches are those whose kernel lives in namespace sgemm::,
     taken in dispatch order; their count must equal the run's
-    trace_total_calls.  Runs on the host, no GPU."""
+    trace_total_calls.  A counter CSV may also be given alone, in place of
+    the trace.  Runs on the host, no GPU."""
     import statistics
 
     cases, total = [], None
@@ -524,7 +525,17 @@ def trace_summary(trace_csv: str, cases_jsonl: str, counters_csv: str | None = N
     def ours(name):
         return "sgemm::" in name
 
-    disp = sorted((r for r in _read_csv(trace_csv) if ours(r["Kernel_Name"])),
+    rows0 = _read_csv(trace_csv)
+    if rows0 and "Counter_Name" in rows0[0]:
+        # A counter CSV given alone: one row per dispatch and counter; its
+        # timestamps (taken under counter collection) stand in for the trace.
+        counters_csv, seen, kept = trace_csv, set(), []
+        for r in rows0:
+            if ours(r["Kernel_Name"]) and r["Dispatch_Id"] not in seen:
+                seen.add(r["Dispatch_Id"])
+                kept.append(r)
+        rows0 = kept
+    disp = sorted((r for r in rows0 if ours(r["Kernel_Name"])),
                   key=lambda r: int(r["Dispatch_Id"]))
     if total is not None and len(disp) != total:
         raise ValueError(f"{len(disp)} library dispatches in the trace, run made {total} calls")

@@ -52,16 +52,23 @@ namespace sgemm {
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Chunk swizzle of row `row` of a k-contiguous slice image with BK floats per
-// row (SWZ = false keeps the plain layout, for measuring what it buys).
+// row (SWZ = false keeps the plain layout, for measuring what it buys).  A
+// 128-bit LDS read is served 16 lanes at a time over 64 four-byte banks, so
+// the 16 rows that 16 consecutive lanes read must land on 16 distinct
+// 16-byte bank groups: rows of 64 B share a 256-B bank line four at a time,
+// rows of 128 B two at a time, and rows of 256 B or more start on the same
+// bank, so their chunk index is XORed with the row mod 16.
 template <int BK, bool SWZ>
 __device__ __forceinline__ int kc_swizzle(int row) {
-  static_assert(BK == 16 || BK == 32, "swizzle is defined for 4 or 8 chunks per row");
+  static_assert(BK == 16 || BK == 32 || BK == 64, "swizzle is defined for 4, 8 or 16 chunks");
   if constexpr (!SWZ)
     return 0;
   else if constexpr (BK == 16)
     return ((row >> 1) ^ ((row >> 3) & 1)) & 3;
-  else
+  else if constexpr (BK == 32)
     return (row ^ ((row >> 3) & 1)) & 7;
+  else
+    return row & 15;
 }
 
 // Word 3 of a raw (untyped, unswizzled) buffer descriptor on CDNA.
@@ -100,6 +107,15 @@ __device__ __forceinline__ void lds_dma(__amdgpu_buffer_rsrc_t r, float *lds, un
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, off, 0, 0, 0);
   else
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 4, off, 0, 0, 0);
+}
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>());
+    static_for<N, I + 1>(f);
+  }
 }
 
 // Host-side limit of the path: every in-range offset of a slice (relative to
@@ -147,8 +163,13 @@ struct SliceGeom {
 // which is what lets a product with fewer 64 x 64 tiles than CUs spread over
 // the whole chip; the order of additions is still fixed for a given call
 // shape.
+//
+// NST: LDS stages.  The loads of slice t+NST go out right after the barrier
+// that ends slice t, into the stage slice t has released, and the barrier
+// that ends slice t+1 waits only for slice t+1 -- NST-1 slices of latency
+// cover.  When K fits NST slices, every slice is in flight from the start.
 template <int BM, int BN, int BK, int WM, int WN, bool SWZ, bool KFULL, int SCHED, bool VA,
-          bool VB, bool TA, bool TB, int KSPLIT = 1>
+          bool VB, bool TA, bool TB, int KSPLIT = 1, int NST = 2>
 __global__ void __launch_bounds__(WM *WN *KSPLIT *kWave)
 mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   constexpr int NWT = WM * WN;       // waves of one k set
@@ -157,7 +178,7 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int KH = BK / 2, G = KH / 4;
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-  static_assert(G >= 2, "BK must be 16 or 32");
+  static_assert(G >= 2, "BK must be 16, 32 or 64");
   static_assert(G % KSPLIT == 0, "k groups must split evenly over the k sets");
   constexpr int GW = G / KSPLIT;  // k groups per slice of one wave
   // A as given has k along its columns; transposed, along its rows.  B the
@@ -165,10 +186,34 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   using GA = SliceGeom<BM, BK, TA, VA, SWZ, NW>;
   using GB = SliceGeom<BN, BK, !TB, VB, SWZ, NW>;
 
-  __shared__ __attribute__((aligned(1024))) float As0[BM * BK];
-  __shared__ __attribute__((aligned(1024))) float As1[BM * BK];
-  __shared__ __attribute__((aligned(1024))) float Bs0[BK * BN];
-  __shared__ __attribute__((aligned(1024))) float Bs1[BK * BN];
+  // One LDS array per stage and operand: with distinct objects the compiler
+  // sees that the loads into one stage do not touch the stage being read,
+  // and adds no wait for them before the operand reads (with the stages in
+  // one array it waits for every load in flight, serialising the pipeline).
+  static_assert(NST >= 2 && NST <= 4, "2 to 4 LDS stages");
+  constexpr int SA = BM * BK, SB = BK * BN;
+  __shared__ __attribute__((aligned(1024))) float As0[SA];
+  __shared__ __attribute__((aligned(1024))) float As1[SA];
+  __shared__ __attribute__((aligned(1024))) float As2[NST > 2 ? SA : 1];
+  __shared__ __attribute__((aligned(1024))) float As3[NST > 3 ? SA : 1];
+  __shared__ __attribute__((aligned(1024))) float Bs0[SB];
+  __shared__ __attribute__((aligned(1024))) float Bs1[SB];
+  __shared__ __attribute__((aligned(1024))) float Bs2[NST > 2 ? SB : 1];
+  __shared__ __attribute__((aligned(1024))) float Bs3[NST > 3 ? SB : 1];
+  auto stage_a = [&](auto S) -> float * {
+    constexpr int i = decltype(S)::value;
+    if constexpr (i == 0) return As0;
+    else if constexpr (i == 1) return As1;
+    else if constexpr (i == 2) return As2;
+    else return As3;
+  };
+  auto stage_b = [&](auto S) -> float * {
+    constexpr int i = decltype(S)::value;
+    if constexpr (i == 0) return Bs0;
+    else if constexpr (i == 1) return Bs1;
+    else if constexpr (i == 2) return Bs2;
+    else return Bs3;
+  };
   // Partial sums of k sets 1 .. KSPLIT-1 for the final reduction.
   constexpr int kRedSlot = NWT * FM * FN * 16 * kWave;
   __shared__ __attribute__((aligned(1024))) float Red[KSPLIT > 1 ? (KSPLIT - 1) * kRedSlot : 1];
@@ -220,8 +265,8 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   // these loads with matrix-core instructions.
   const int nk = (p.K + BK - 1) / BK;
   auto dma = [&](auto S, int t) {
-    float *as = S.value ? As1 : As0;
-    float *bs = S.value ? Bs1 : Bs0;
+    float *as = stage_a(S);
+    float *bs = stage_b(S);
     const int k0 = t < nk ? t * BK : 0;
     const int records = t < nk ? kBufferRecords : 0;
     // K tail (not KFULL): an operand whose k runs along its stored rows ends
@@ -269,8 +314,8 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     f32x4 b[FN];
   };
   auto read_ops = [&](auto S, int g, Ops &o) {
-    const float *as = S.value ? As1 : As0;
-    const float *bs = S.value ? Bs1 : Bs0;
+    const float *as = stage_a(S);
+    const float *bs = stage_b(S);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       if constexpr (TA) {
@@ -309,7 +354,6 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   };
 
   using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
   Ops cur, nxt;
 
   // Instruction interleaving inside one group (SCHED = 1): first one
@@ -335,11 +379,12 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     }
   };
 
-  // Slice t lives in stage S; slice t+1 (if any) is already on its way to
-  // stage S^1.
+  // Slice t lives in stage S = t % NST; slices t+1 .. t+NST-1 are already on
+  // their way to the other stages.
+  constexpr int kLoadsPerSlice = GA::NBW + GB::NBW;  // per wave
   auto slice = [&](auto S, int t) {
     constexpr int s = decltype(S)::value;
-    using SN = std::integral_constant<int, s ^ 1>;
+    using SN = std::integral_constant<int, (s + 1) % NST>;
 #pragma unroll
     for (int g = 0; g < GW; ++g) {
       if (g + 1 < GW) {
@@ -347,9 +392,10 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         mma(cur);
         interleave(std::false_type());
       } else {
-        // All reads of stage S are done and slice t+1 has landed in S^1.
-        dma_barrier();
-        dma(S, t + 2);
+        // All reads of stage S are done and slice t+1 has landed (only the
+        // loads of slices t+2 .. t+NST-1 may still be in flight).
+        dma_barrier_keep<(NST - 2) * kLoadsPerSlice>();
+        dma(S, t + NST);
         read_ops(SN(), 0, nxt);  // harmless if there is no slice t+1
         mma(cur);
         interleave(std::true_type());
@@ -358,13 +404,14 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     }
   };
 
-  dma(S0(), 0);
-  dma(S1(), 1);
-  dma_barrier_keep<GA::NBW + GB::NBW>();  // slice 0 has landed; slice 1 may still fly
+  static_for<NST>([&](auto S) { dma(S, decltype(S)::value); });
+  // Slice 0 has landed; slices 1 .. NST-1 may still fly.
+  dma_barrier_keep<(NST - 1) * kLoadsPerSlice>();
   read_ops(S0(), 0, cur);
-  for (int t = 0; t < nk; t += 2) {
-    slice(S0(), t);
-    if (t + 1 < nk) slice(S1(), t + 1);
+  for (int t = 0; t < nk; t += NST) {
+    static_for<NST>([&](auto S) {
+      if (decltype(S)::value == 0 || t + decltype(S)::value < nk) slice(S, t + decltype(S)::value);
+    });
   }
   // The last slices issued loads past K (zero-filling, no memory traffic);
   // let them retire before the work-group gives up its LDS.
@@ -435,72 +482,72 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool SWZ, int SCHED, bool VA, bool VB, bool TA,
-          bool TB, int KSPLIT>
+          bool TB, int KSPLIT, int NST>
 inline void launch_dma_kernel(const GemmArgs &p, hipStream_t stream, int group_m) {
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const dim3 grid((unsigned)((long)tiles_m * tiles_n * p.batch)),
       block(WM * WN * KSPLIT * kWave);
   if (p.K % BK == 0)
     hipLaunchKernelGGL(
-        (mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, true, SCHED, VA, VB, TA, TB, KSPLIT>),
+        (mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, true, SCHED, VA, VB, TA, TB, KSPLIT, NST>),
         grid, block, 0, stream, p, tiles_m, tiles_n, group_m);
   else
     hipLaunchKernelGGL(
-        (mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, false, SCHED, VA, VB, TA, TB, KSPLIT>),
+        (mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, false, SCHED, VA, VB, TA, TB, KSPLIT, NST>),
         grid, block, 0, stream, p, tiles_m, tiles_n, group_m);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool SWZ, int SCHED, bool TA, bool TB,
-          int KSPLIT>
+          int KSPLIT, int NST>
 inline void launch_dma_widths(const GemmArgs &p, bool va, bool vb, hipStream_t stream,
                               int group_m) {
   if (va && vb)
-    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true, TA, TB, KSPLIT>(p, stream,
-                                                                                 group_m);
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true, TA, TB, KSPLIT, NST>(
+        p, stream, group_m);
   else if (va)
-    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, false, TA, TB, KSPLIT>(p, stream,
-                                                                                  group_m);
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, false, TA, TB, KSPLIT, NST>(
+        p, stream, group_m);
   else if (vb)
-    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, true, TA, TB, KSPLIT>(p, stream,
-                                                                                  group_m);
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, true, TA, TB, KSPLIT, NST>(
+        p, stream, group_m);
   else
-    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, false, TA, TB, KSPLIT>(p, stream,
-                                                                                   group_m);
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, false, TA, TB, KSPLIT, NST>(
+        p, stream, group_m);
 }
 
 // Plain layout (no transposes).  WIDE_ONLY instantiates only the 16-byte-load
 // form; the caller guarantees va && vb.
 template <int BM, int BN, int BK, int WM, int WN, bool SWZ = true, int SCHED = 1,
-          bool WIDE_ONLY = false, int KSPLIT = 1>
+          bool WIDE_ONLY = false, int KSPLIT = 1, int NST = 2>
 inline hipError_t launch_dma_cfg(const GemmArgs &p, bool va, bool vb, hipStream_t stream,
                                  int group_m = 8) {
   if constexpr (WIDE_ONLY) {
     if (!(va && vb)) return hipErrorInvalidValue;
-    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true, false, false, KSPLIT>(
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true, false, false, KSPLIT, NST>(
         p, stream, group_m);
   } else {
-    launch_dma_widths<BM, BN, BK, WM, WN, SWZ, SCHED, false, false, KSPLIT>(p, va, vb, stream,
-                                                                            group_m);
+    launch_dma_widths<BM, BN, BK, WM, WN, SWZ, SCHED, false, false, KSPLIT, NST>(p, va, vb,
+                                                                                 stream, group_m);
   }
   return hipGetLastError();
 }
 
 // Any layout.
-template <int BM, int BN, int BK, int WM, int WN, int KSPLIT = 1>
+template <int BM, int BN, int BK, int WM, int WN, int KSPLIT = 1, int NST = 2>
 inline hipError_t launch_dma_general(const GemmArgs &p, bool ta, bool tb, bool va, bool vb,
                                      hipStream_t stream, int group_m = 8) {
   if (!ta && !tb)
-    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, false, false, KSPLIT>(p, va, vb, stream,
-                                                                         group_m);
+    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, false, false, KSPLIT, NST>(p, va, vb, stream,
+                                                                              group_m);
   else if (!ta)
-    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, false, true, KSPLIT>(p, va, vb, stream,
-                                                                        group_m);
+    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, false, true, KSPLIT, NST>(p, va, vb, stream,
+                                                                             group_m);
   else if (!tb)
-    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, true, false, KSPLIT>(p, va, vb, stream,
-                                                                        group_m);
+    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, true, false, KSPLIT, NST>(p, va, vb, stream,
+                                                                             group_m);
   else
-    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, true, true, KSPLIT>(p, va, vb, stream,
-                                                                       group_m);
+    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, true, true, KSPLIT, NST>(p, va, vb, stream,
+                                                                            group_m);
   return hipGetLastError();
 }
 
