@@ -78,6 +78,9 @@ def load_library(path: str = LIB_PATH):
     lib.sgemm_run_bf16x3_ex.argtypes = [ci, ci, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp,
                                         i64, vp, i64, vp]
     lib.sgemm_run_bf16x3_ex.restype = ci
+    lib.sgemm_run_bf16x3_ex_noalloc.argtypes = [ci, ci, i64, i64, i64, f32, vp, i64, vp, i64,
+                                                f32, vp, i64, vp]
+    lib.sgemm_run_bf16x3_ex_noalloc.restype = ci
     lib.vector_add.argtypes = [i64, vp, vp, vp, vp]
     lib.vector_add.restype = ci
     lib.sgemm_mfma_ceiling.argtypes = [ci, ci, vp, i64, ctypes.POINTER(ctypes.c_double), vp]
@@ -177,6 +180,14 @@ def sgemm_run_bf16x3_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
     _check("sgemm_run_bf16x3_ex", load_library().sgemm_run_bf16x3_ex(
         int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
         float(beta), _ptr(C), ldc, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def sgemm_run_bf16x3_ex_noalloc(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                stream=None) -> None:
+    """sgemm_run_bf16x3_ex with the library-held split buffer (no workspace)."""
+    _check("sgemm_run_bf16x3_ex_noalloc", load_library().sgemm_run_bf16x3_ex_noalloc(
+        int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
+        float(beta), _ptr(C), ldc, _stream(stream)))
 
 
 def vector_add(n, A, B, C, stream=None) -> None:

@@ -7,6 +7,7 @@
 #include <cstring>
 #include <mutex>
 
+#include "api_internal.hpp"
 #include "dispatch.hpp"
 #include "sgemm.h"
 #include "sgemm_bf16x3.h"
@@ -267,10 +268,17 @@ int64_t sgemm_bf16x3_workspace_size(int64_t M, int64_t N, int64_t K) {
   return 6 * Kp * (M + N);  // three 2-byte planes of each operand
 }
 
-int sgemm_run_bf16x3_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
-                        const float *A, int64_t lda, const float *B, int64_t ldb, float beta,
-                        float *C, int64_t ldc, void *workspace, int64_t workspace_bytes,
-                        void *stream) {
+}  // extern "C"
+
+namespace sgemm_api {
+
+// The argument checks of sgemm_run_bf16x3_ex other than those of the
+// workspace; *need receives the workspace bytes the call needs (0 when it
+// reads neither A, B nor the workspace).
+int bf16x3_ex_check(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                    const float *A, int64_t lda, const float *B, int64_t ldb, const float *C,
+                    int64_t ldc, int64_t *need) {
+  *need = 0;
   if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1)) return SGEMM_ERR_INVALID_VALUE;
   if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_INVALID_VALUE;
   const int64_t a_cols = transA ? M : K, b_cols = transB ? K : N;
@@ -280,13 +288,31 @@ int sgemm_run_bf16x3_ex(int transA, int transB, int64_t M, int64_t N, int64_t K,
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return SGEMM_ERR_TOO_LARGE;
   if (!grid_fits(M, N, 1, 64, 256)) return SGEMM_ERR_TOO_LARGE;
   const bool reads_ab = M > 0 && N > 0 && K > 0 && alpha != 0.f;
-  int64_t need = 0;
   if (reads_ab) {
-    need = sgemm_bf16x3_workspace_size(M, N, K);
-    if (need < 0) return (int)need;
+    const int64_t w = sgemm_bf16x3_workspace_size(M, N, K);
+    if (w < 0) return (int)w;
+    *need = w;
   }
   if (M > 0 && N > 0 && !C) return SGEMM_ERR_INVALID_VALUE;
   if (reads_ab && (!A || !B)) return SGEMM_ERR_INVALID_VALUE;
+  return SGEMM_OK;
+}
+
+bool ready() { return g_ready.load(std::memory_order_acquire) != 0; }
+
+}  // namespace sgemm_api
+
+extern "C" {
+
+int sgemm_run_bf16x3_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                        const float *A, int64_t lda, const float *B, int64_t ldb, float beta,
+                        float *C, int64_t ldc, void *workspace, int64_t workspace_bytes,
+                        void *stream) {
+  int64_t need = 0;
+  const int chk =
+      sgemm_api::bf16x3_ex_check(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc, &need);
+  if (chk != SGEMM_OK) return chk;
+  const bool reads_ab = need > 0;
   if (reads_ab && (!workspace || !aligned16(workspace) || workspace_bytes < need))
     return SGEMM_ERR_INVALID_VALUE;
   if (!g_ready.load(std::memory_order_acquire)) return SGEMM_ERR_NOT_INITIALIZED;

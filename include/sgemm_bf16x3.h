@@ -72,6 +72,35 @@ int sgemm_run_bf16x3_ex(int transA, int transB, int64_t M, int64_t N, int64_t K,
                         float *C, int64_t ldc, void *workspace, int64_t workspace_bytes,
                         void *stream);
 
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the same
+ * call as sgemm_run_bf16x3_ex, without the workspace arguments.  The split
+ * planes go to a buffer the library holds on each GPU it runs on
+ * (SGEMM_BF16X3_NOALLOC_MAX_BYTES, 64 MiB, kept until the process ends and
+ * set up by the runtime when this entry point is first called on that GPU);
+ * the call itself allocates nothing and calls no allocating routine.
+ *
+ * Limit: a call whose workspace, sgemm_bf16x3_workspace_size(M, N, K),
+ * exceeds SGEMM_BF16X3_NOALLOC_MAX_BYTES returns SGEMM_ERR_TOO_LARGE before
+ * anything is enqueued (2048 x 2048 x 2048 needs 50.3 MB and fits; 4096^3
+ * does not).  Every other status, check and result is exactly that of
+ * sgemm_run_bf16x3_ex with a large enough workspace: the results are bit for
+ * bit the same.  SGEMM_ERR_HIP if the buffer's device address cannot be
+ * looked up.
+ *
+ * Every call on one GPU shares that GPU's buffer: calls that overlap on one
+ * GPU (in flight together on different streams, or from different host
+ * threads) race and must be ordered by the caller.  Each call rewrites
+ * every byte of the buffer it reads, so nothing left by an earlier call
+ * affects a later one.
+ */
+#define SGEMM_BF16X3_NOALLOC_MAX_BYTES (64ll << 20)
+
+int sgemm_run_bf16x3_ex_noalloc(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                                float alpha, const float *A, int64_t lda, const float *B,
+                                int64_t ldb, float beta, float *C, int64_t ldc, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
