@@ -14,7 +14,7 @@ clocks have settled) and reported under "secondary".
 
 The other modes print one JSON line per case: every workload with oracle
 times (--table), the general form and strided batches (--general), small
-products with and without the k-split 32 x 32 tile (--small), one
+products with sgemm_run's tile and every forced tile (--small), one
 GPU's share of 8192^3 split by rows over 1-8 GPUs (--shards), the pages'
 progression (--ladder), the vector add (--vector-add), the bfloat16 split
 path (--bf16x3, --bf16x3-general), and the copy that calibrates the HBM
@@ -400,54 +400,41 @@ def general_table(settle: float) -> list[dict]:
     return rows
 
 
-# Products with few 64 x 64 tiles: (M, N, K).  The last two sit on either
-# side of the point where sgemm_run switches to the k-split 32 x 32 tile.
-SMALL = ((256, 256, 256), (300, 260, 100), (512, 512, 512), (768, 768, 768),
-         (640, 640, 2048), (1000, 130, 2048), (768, 1024, 512), (832, 1024, 512))
+# Tile sweep: (M, N, K, lda).  Small products, where the count of tiles
+# decides, and medium ones on either side of each switch of sgemm_run's tile
+# rule; 1000 x 1500 x 777 is the ragged workload (A rows not 16-byte aligned).
+SMALL = ((256, 256, 256, 256), (300, 260, 100, 100), (512, 512, 512, 512),
+         (768, 768, 768, 768), (640, 640, 2048, 2048), (1000, 130, 2048, 2048),
+         (768, 1024, 512, 512), (832, 1024, 512, 512), (1024, 1024, 1024, 1024),
+         (1000, 1500, 776, 776), (1000, 1500, 777, 777), (1536, 1536, 1536, 1536),
+         (2048, 2048, 2048, 2048), (3072, 3072, 1024, 1024), (4096, 4096, 1024, 1024))
+SMALL_TILES = ("mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_32x64", "mfma_32")
 
 
-def small_table(steps: int) -> list[dict]:
-    """sgemm_run on the SMALL shapes with the 64 x 64 tile forced, then with
-    the tile sgemm_run chooses; HIP-event time per call over `steps` calls
-    (which for the shortest includes the host's launch cost; a kernel trace
-    gives the kernels' own durations)."""
-    import numpy as np
-    import torch
-
-    import dense_fp32_matrix_03_amd as sg
+def small_table(steps: int, settle: float) -> list[dict]:
+    """sgemm_run and every forced tile on the SMALL shapes: HIP-event time
+    per call over `steps` back-to-back calls after `settle` seconds of
+    untimed calls (for the shortest this includes the host's launch cost; a
+    kernel trace of the run gives the kernels' own durations through
+    --trace-summary).  One JSON line per shape and tile."""
     from dense_fp32_matrix_03_amd import inputs
 
-    rows = []
-    stream = torch.cuda.current_stream()
-    h = stream.cuda_stream
-    for M, N, K in SMALL:
-        g = np.random.default_rng(M + N + K)
-        dA = torch.from_numpy(inputs.uniform(g, (M, K))).cuda()
-        dB = torch.from_numpy(inputs.uniform(g, (K, N))).cuda()
-        dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
-        for variant in ("mfma_64", "mfma"):
-            def step():
-                sg.sgemm_run_variant(variant, M, N, K, dA, K, dB, N, dC, N, h)
+    import dense_fp32_matrix_03_amd as sg
 
-            for _ in range(10):
-                step()
-            torch.cuda.synchronize()
-            t0 = torch.cuda.Event(enable_timing=True)
-            t1 = torch.cuda.Event(enable_timing=True)
-            t0.record(stream)
-            for _ in range(steps):
-                step()
-            t1.record(stream)
-            torch.cuda.synchronize()
-            ms = t0.elapsed_time(t1) / steps
-            r = {"M": M, "N": N, "K": K, "variant": sg.sgemm_variant_name(sg.VARIANTS[variant]),
-                 "calls": 10 + steps, "us": round(ms * 1e3, 2),
-                 "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2),
-                 "output_finite": bool(torch.isfinite(dC).all().item())}
+    rows = []
+    for M, N, K, lda in SMALL:
+        w = inputs.Workload(f"sgemm_{M}x{N}x{K}_uniform_seed{M + N + K}", M, N, K, "uniform",
+                            M + N + K, lda, N, N, "full")
+        for variant in SMALL_TILES:
+            v = sg.VARIANTS[variant]
+            ms, finite = time_gpu(w, v, steps, 10, warm_seconds=settle)
+            r = {"case": sg.sgemm_variant_name(v), "M": M, "N": N, "K": K, "lda": lda,
+                 "variant": sg.sgemm_variant_name(v), "us": round(ms * 1e3, 3),
+                 "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2), "output_finite": finite,
+                 **trace_fields()}
             print(json.dumps(r), flush=True)
             rows.append(r)
-        del dA, dB, dC
-    torch.cuda.empty_cache()
+    print(json.dumps({"trace_total_calls": _CALLS[0]}), flush=True)
     return rows
 
 
@@ -765,8 +752,8 @@ def main(argv=None) -> int:
                          "and all threads; 8192^3 single-thread extrapolated from the "
                          "2048^3 rate) and print one JSON line per workload")
     ap.add_argument("--small", action="store_true",
-                    help="time products with few 64x64 tiles with the 64x64 tile forced and "
-                         "with the tile sgemm_run picks (one JSON line each)")
+                    help="time sgemm_run and every forced tile on small and medium products "
+                         "(one JSON line each)")
     ap.add_argument("--shards", action="store_true",
                     help="time one GPU's share of 8192^3 split by rows of C over 1, 2, 4 "
                          "and 8 GPUs (single GPU; one JSON line each)")
@@ -845,7 +832,7 @@ def main(argv=None) -> int:
         sg.sgemm_destroy()
         return 0
     if a.small:
-        small_table(max(a.steps, 100))
+        small_table(max(a.steps, 100), min(a.settle, 0.1))
         sg.sgemm_destroy()
         return 0
     if a.shards:

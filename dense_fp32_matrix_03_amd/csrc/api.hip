@@ -68,11 +68,12 @@ constexpr int64_t kMaxBf16x3K = int64_t(1) << 21;
 constexpr int64_t kMaxBf16x3Split = int64_t(1) << 34;
 
 // Whether `batch` products of M x N, one `threads`-wide work-group per
-// tile x tile block of C, fit one launch.  The matrix-core kernels use at
-// most 256 threads per 64 x 64 block; the vector-FMA rungs 256 threads per
-// 16 x 16 block (or the equivalent).
-bool grid_fits(int64_t M, int64_t N, int64_t batch, int64_t tile, int64_t threads) {
-  const int64_t tiles = ((M + tile - 1) / tile) * ((N + tile - 1) / tile);
+// bm x bn block of C, fit one launch.  sgemm_run and the general form pick a
+// tile whose launch fits (the 128 x 128 tile, 128 threads per 64 x 64 block,
+// always does once 256 per 64 x 64 block fit); the vector-FMA rungs use 256
+// threads per 16 x 16 block (or the equivalent).
+bool grid_fits(int64_t M, int64_t N, int64_t batch, int64_t bm, int64_t bn, int64_t threads) {
+  const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   return batch == 0 || tiles <= kMaxWorkItems / threads / batch;
 }
 
@@ -83,7 +84,7 @@ int check_args(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, con
   if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
     return SGEMM_ERR_INVALID_VALUE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return SGEMM_ERR_TOO_LARGE;
-  if (!grid_fits(M, N, 1, 64, 256)) return SGEMM_ERR_TOO_LARGE;
+  if (!grid_fits(M, N, 1, 64, 64, 256)) return SGEMM_ERR_TOO_LARGE;
   if (M == 0 || N == 0) return SGEMM_OK;
   if (!C) return SGEMM_ERR_INVALID_VALUE;
   if (K > 0 && (!A || !B)) return SGEMM_ERR_INVALID_VALUE;
@@ -119,10 +120,15 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
   if (variant < 0 || variant >= SGEMM_NUM_VARIANTS) return SGEMM_ERR_INVALID_VALUE;
   int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc);
   if (rc != SGEMM_OK) return rc;
-  if (variant <= SGEMM_VARIANT_DBUF && !grid_fits(M, N, 1, 16, 256)) return SGEMM_ERR_TOO_LARGE;
-  // The forced 32 x 32 tile runs 256 threads per 32 x 32 block (sgemm_run
-  // only picks it for products far below this limit).
-  if (variant == SGEMM_VARIANT_MFMA_32 && !grid_fits(M, N, 1, 32, 256)) return SGEMM_ERR_TOO_LARGE;
+  if (variant <= SGEMM_VARIANT_DBUF && !grid_fits(M, N, 1, 16, 16, 256)) return SGEMM_ERR_TOO_LARGE;
+  // Forced tiles: 512 threads per 64 x 64 block, 256 per 32 x 64 or 32 x 32
+  // block (sgemm_run only picks a tile whose launch fits).
+  if (variant == SGEMM_VARIANT_MFMA_64 && !grid_fits(M, N, 1, 64, 64, 512))
+    return SGEMM_ERR_TOO_LARGE;
+  if (variant == SGEMM_VARIANT_MFMA_32X64 && !grid_fits(M, N, 1, 32, 64, 256))
+    return SGEMM_ERR_TOO_LARGE;
+  if (variant == SGEMM_VARIANT_MFMA_32 && !grid_fits(M, N, 1, 32, 32, 256))
+    return SGEMM_ERR_TOO_LARGE;
   if (!g_ready.load(std::memory_order_acquire)) return SGEMM_ERR_NOT_INITIALIZED;
   if (M == 0 || N == 0) return SGEMM_OK;
   DeviceInfo di;
@@ -149,7 +155,10 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
     const bool vb = aligned16(B) && ldb % 4 == 0 && N % 4 == 0;
     using sgemm::MfmaPath;
     using sgemm::MfmaTile;
-    const MfmaTile autotile = sgemm::choose_mfma_tile(M, N, di.cus);
+    const sgemm::TileChoice autotile = sgemm::choose_mfma_tile(M, N, di.cus);
+    // A forced tile keeps the K-slice rule of the automatic choice, so it
+    // gives sgemm_run's bits whenever sgemm_run picks the same tile.
+    auto forced = [&](MfmaTile t) { return sgemm::with_slice_rule(t, M, N, di.cus); };
     switch (variant) {
       case SGEMM_VARIANT_NAIVE:
       case SGEMM_VARIANT_LDS:
@@ -158,16 +167,19 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
         err = sgemm::launch_valu(variant - SGEMM_VARIANT_NAIVE, p, va, vb, s);
         break;
       case SGEMM_VARIANT_MFMA_256:
-        err = sgemm::launch_mfma(MfmaTile::T256, MfmaPath::Auto, p, va, vb, s);
+        err = sgemm::launch_mfma(forced(MfmaTile::T256), MfmaPath::Auto, p, va, vb, s);
         break;
       case SGEMM_VARIANT_MFMA_128:
-        err = sgemm::launch_mfma(MfmaTile::T128, MfmaPath::Auto, p, va, vb, s);
+        err = sgemm::launch_mfma(forced(MfmaTile::T128), MfmaPath::Auto, p, va, vb, s);
         break;
       case SGEMM_VARIANT_MFMA_64:
-        err = sgemm::launch_mfma(MfmaTile::T64, MfmaPath::Auto, p, va, vb, s);
+        err = sgemm::launch_mfma(forced(MfmaTile::T64), MfmaPath::Auto, p, va, vb, s);
+        break;
+      case SGEMM_VARIANT_MFMA_32X64:
+        err = sgemm::launch_mfma(forced(MfmaTile::T32x64), MfmaPath::Auto, p, va, vb, s);
         break;
       case SGEMM_VARIANT_MFMA_32:
-        err = sgemm::launch_mfma(MfmaTile::T32, MfmaPath::Auto, p, va, vb, s);
+        err = sgemm::launch_mfma(forced(MfmaTile::T32), MfmaPath::Auto, p, va, vb, s);
         break;
       case SGEMM_VARIANT_MFMA_STAGED:
         err = sgemm::launch_mfma(autotile, MfmaPath::Staged, p, va, vb, s);
@@ -208,7 +220,7 @@ int sgemm_run_strided_batched(int transA, int transB, int64_t M, int64_t N, int6
       ldc < (N > 1 ? N : 1))
     return SGEMM_ERR_INVALID_VALUE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim || batch > kMaxDim) return SGEMM_ERR_TOO_LARGE;
-  if (!grid_fits(M, N, batch, 64, 256)) return SGEMM_ERR_TOO_LARGE;
+  if (!grid_fits(M, N, batch, 64, 64, 256)) return SGEMM_ERR_TOO_LARGE;
   const bool reads_ab = K > 0 && alpha != 0.f;
   if (M > 0 && N > 0 && batch > 0) {
     if (!C) return SGEMM_ERR_INVALID_VALUE;
@@ -246,7 +258,7 @@ int sgemm_run_strided_batched(int transA, int transB, int64_t M, int64_t N, int6
     // dimensions, and a stored width that is a multiple of 4.
     const bool va = aligned16(A) && lda % 4 == 0 && strideA % 4 == 0 && a_cols % 4 == 0;
     const bool vb = aligned16(B) && ldb % 4 == 0 && strideB % 4 == 0 && b_cols % 4 == 0;
-    const sgemm::MfmaTile tile = sgemm::choose_mfma_tile(M, N, di.cus, batch);
+    const sgemm::TileChoice tile = sgemm::choose_mfma_tile(M, N, di.cus, batch);
     err = sgemm::launch_mfma_general(tile, p, transA, transB, va, vb, s);
     if (err == hipErrorInvalidValue) return SGEMM_ERR_TOO_LARGE;
   }
@@ -286,7 +298,7 @@ int bf16x3_ex_check(int transA, int transB, int64_t M, int64_t N, int64_t K, flo
       ldc < (N > 1 ? N : 1))
     return SGEMM_ERR_INVALID_VALUE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return SGEMM_ERR_TOO_LARGE;
-  if (!grid_fits(M, N, 1, 64, 256)) return SGEMM_ERR_TOO_LARGE;
+  if (!grid_fits(M, N, 1, 64, 64, 256)) return SGEMM_ERR_TOO_LARGE;
   const bool reads_ab = M > 0 && N > 0 && K > 0 && alpha != 0.f;
   if (reads_ab) {
     const int64_t w = sgemm_bf16x3_workspace_size(M, N, K);
@@ -356,7 +368,7 @@ int sgemm_run_bf16x3_ex(int transA, int transB, int64_t M, int64_t N, int64_t K,
       p.ldc = ldc;
       p.alpha = alpha;
       p.beta = beta;
-      err = sgemm::launch_bf16x3_gemm(sgemm::choose_mfma_tile(M, N, di.cus), p, s);
+      err = sgemm::launch_bf16x3_gemm(p, di.cus, s);
       if (err == hipErrorInvalidValue) return SGEMM_ERR_TOO_LARGE;
     }
   }
@@ -430,11 +442,12 @@ const char *sgemm_variant_name(int variant) {
     case SGEMM_VARIANT_MFMA: return "mfma_auto";
     case SGEMM_VARIANT_MFMA_256: return "mfma_256x256";
     case SGEMM_VARIANT_MFMA_128: return "mfma_128x128";
-    case SGEMM_VARIANT_MFMA_64: return "mfma_64x64";
+    case SGEMM_VARIANT_MFMA_64: return "mfma_64x64_ksplit2";
     case SGEMM_VARIANT_MFMA_32: return "mfma_32x32_ksplit4";
     case SGEMM_VARIANT_MFMA_STAGED: return "mfma_register_staged";
     case SGEMM_VARIANT_MFMA_UNPADDED: return "mfma_unpadded_lds";
     case SGEMM_VARIANT_MFMA_DWORD: return "mfma_dword_loads";
+    case SGEMM_VARIANT_MFMA_32X64: return "mfma_32x64_ksplit2";
     default: return nullptr;
   }
 }

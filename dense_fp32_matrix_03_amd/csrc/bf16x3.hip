@@ -530,14 +530,17 @@ static hipError_t launch_bf16x3_cfg(const Bf16x3Args &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bf16x3_gemm(MfmaTile tile, const Bf16x3Args &p, hipStream_t stream) {
-  switch (tile) {
-    case MfmaTile::T256: return launch_bf16x3_cfg<256, 256, 16, 2, 4, 0, 2>(p, stream);
-    case MfmaTile::T128: return launch_bf16x3_cfg<128, 128, 32, 2, 4, 1, 2>(p, stream);
-    case MfmaTile::T64:
-    case MfmaTile::T32: return launch_bf16x3_cfg<64, 64, 32, 2, 2, 1, 2>(p, stream);
-  }
-  return hipErrorInvalidValue;
+// Tile of the six-product kernel: the largest of 256 x 256 and 128 x 128
+// that still gives every compute unit a work-group and whose tiles lie at
+// least 3/4 inside C; else 64 x 64.
+hipError_t launch_bf16x3_gemm(const Bf16x3Args &p, int cus, hipStream_t stream) {
+  auto tiles = [&](long t) { return (double)((p.M + t - 1) / t) * ((p.N + t - 1) / t); };
+  auto good = [&](long t) {
+    return tiles(t) >= cus && 4.0 * p.M * p.N >= 3.0 * tiles(t) * t * t;
+  };
+  if (good(256)) return launch_bf16x3_cfg<256, 256, 16, 2, 4, 0, 2>(p, stream);
+  if (good(128)) return launch_bf16x3_cfg<128, 128, 32, 2, 4, 1, 2>(p, stream);
+  return launch_bf16x3_cfg<64, 64, 32, 2, 2, 1, 2>(p, stream);
 }
 
 // One-instruction probe of v_mfma_f32_32x32x16_bf16: A is 32 x 16 and B is

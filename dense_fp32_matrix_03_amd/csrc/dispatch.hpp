@@ -7,10 +7,19 @@
 
 namespace sgemm {
 
-// Block tiles of the matrix-core kernels.  T32 is a 32 x 32 tile whose
-// work-group splits K over four waves (one per SIMD), for products whose
-// 64 x 64 tiles would leave a quarter of the compute units or more idle.
-enum class MfmaTile { T256, T128, T64, T32 };
+// Block tiles of the matrix-core kernels (mfma_configs.hpp gives their wave
+// grids): 256 x 256, 128 x 128, 64 x 64 (K split over two sets of waves),
+// 32 x 64 (two k sets) and 32 x 32 (four k sets).
+enum class MfmaTile { T256, T128, T64, T32x64, T32 };
+
+// A tile and its K-slice length: long_k selects 64-float slices, which the
+// four-wave tiles (32 x 64, 32 x 32) take when all their work-groups fit one
+// round on the compute units (no second work-group per CU hides the
+// per-slice barrier, and half as many slices halve its cost).
+struct TileChoice {
+  MfmaTile tile;
+  bool long_k;
+};
 
 // Which matrix-core kernel:
 //  Auto      buffer-to-LDS loads (16 bytes per lane where va / vb, else
@@ -21,20 +30,29 @@ enum class MfmaTile { T256, T128, T64, T32 };
 //            no A row padding), to measure what that layout buys.
 enum class MfmaPath { Auto, Staged, Unpadded };
 
-// Largest tile that still gives at least one work-group per compute unit
-// over `batch` products; T32 when 64 x 64 tiles would fill at most 3/4 of
-// the compute units.
-MfmaTile choose_mfma_tile(long M, long N, int cus, long batch = 1);
+// The tile for `batch` products of M x N on `cus` compute units: the one
+// that wastes the least matrix-core time to partly filled rounds of
+// work-groups and to tile area outside C, preferring the larger tile when
+// two come within 3% of each other.
+TileChoice choose_mfma_tile(long M, long N, int cus, long batch = 1);
+
+// `tile` with the K-slice length choose_mfma_tile would give it.
+TileChoice with_slice_rule(MfmaTile tile, long M, long N, int cus, long batch = 1);
 
 // Matrix-core product.  va / vb: A / B qualify for 128-bit loads.
-hipError_t launch_mfma(MfmaTile tile, MfmaPath path, const GemmArgs &p, bool va, bool vb,
+hipError_t launch_mfma(TileChoice tile, MfmaPath path, const GemmArgs &p, bool va, bool vb,
                        hipStream_t stream);
 
 // General product C = alpha op(A) op(B) + beta C over p.batch products on
 // the buffer-to-LDS kernel (ta / tb: A / B stored transposed).  Returns
 // hipErrorInvalidValue if a slice's offsets do not fit a buffer descriptor.
-hipError_t launch_mfma_general(MfmaTile tile, const GemmArgs &p, bool ta, bool tb, bool va,
+hipError_t launch_mfma_general(TileChoice tile, const GemmArgs &p, bool ta, bool tb, bool va,
                                bool vb, hipStream_t stream);
+
+// Register-staged kernel (mfma_gemm.hpp) on a 256, 128 or 64 tile (others
+// take 64); padded = false drops its A row padding.
+hipError_t launch_staged(MfmaTile tile, bool padded, const GemmArgs &p, bool va, bool vb,
+                         hipStream_t stream);
 
 // C = beta * C over p.batch products (zeros when beta == 0; C not read).
 hipError_t launch_scale(const GemmArgs &p, hipStream_t stream);
@@ -66,9 +84,10 @@ struct Bf16x3Args {
 hipError_t launch_split(bool ta, bool tb, const float *A, long lda, const float *B, long ldb,
                         int M, int N, int K, int Kp, void *wa, void *wb, hipStream_t stream);
 
-// C = alpha (sum of the six piece products over the planes) + beta C.  hipErrorInvalidValue
-// if a slice's offsets do not fit a buffer descriptor.
-hipError_t launch_bf16x3_gemm(MfmaTile tile, const Bf16x3Args &p, hipStream_t stream);
+// C = alpha (sum of the six piece products over the planes) + beta C, on a
+// tile chosen for `cus` compute units.  hipErrorInvalidValue if a slice's
+// offsets do not fit a buffer descriptor.
+hipError_t launch_bf16x3_gemm(const Bf16x3Args &p, int cus, hipStream_t stream);
 
 // One-instruction probe of the bfloat16 32x32x16 matrix instruction.
 hipError_t launch_bf16_probe(const float *A, const float *B, float *C, hipStream_t stream);

@@ -1,105 +1,109 @@
-// mfma_kernels.hip -- the configurations of the matrix-core kernels that the
-// library dispatches to, and the one-instruction layout probe.
+// mfma_kernels.hip -- the choice of matrix-core configuration for a call,
+// the dispatch to the per-layout launchers (mfma_configs.hpp,
+// mfma_layout_*.hip) and the register-staged fallback, and the
+// one-instruction layout probe.
+#include <math.h>
+
 #include "common.hpp"
 #include "dispatch.hpp"
-#include "mfma_dma.hpp"
-#include "mfma_gemm.hpp"
+#include "mfma_configs.hpp"
 
 namespace sgemm {
 
-// Tile configurations (block tile, K slice, wave grid), from a sweep over
-// square problems of 1024 .. 8192 on MI355X:
-//   T256  256 x 256 x 32, 2 x 4 waves of 128 x 64  (two waves per SIMD)
-//   T128  128 x 128 x 32, 4 x 2 waves of  32 x 64  (two waves per SIMD;
-//         the register-staged kernel keeps 2 x 2 waves of 64 x 64)
-//   T64    64 x  64 x 32, 2 x 2 waves of  32 x 32
-//   T32    32 x  32 x 32, 4 waves on the same 32 x 32 block, each taking
-//         one of the four k groups of every slice (KSPLIT = 4); for
-//         products with at most 3/4 as many 64 x 64 tiles as CUs it spreads
-//         the work over four times as many work-groups, each on four SIMDs
-//         (512^3: 11.7 -> 7.3 us; 640 x 640 x 2048: 35.4 -> 26.5 us).
-// At 2048^3 (one 128 x 128 tile per CU) eight waves instead of four took the
-// buffer-to-LDS kernel from 140.7 to 144.9 TFLOP/s; at 4096^3 both give 150.5.
-// WIDE_ONLY: only the 16-byte-load forms are instantiated (the caller
-// guarantees va && vb).  DWM x DWN: wave grid of the buffer-to-LDS kernel.
-template <int BM, int BN, int BK, int WM, int WN, bool WIDE_ONLY = false, int DWM = WM,
-          int DWN = WN>
-static hipError_t launch_tile(MfmaPath path, const GemmArgs &p, bool va, bool vb,
-                              hipStream_t stream) {
-  constexpr int kStoreGroup = 1;  // staged kernel: write the next slice after group 1 of 4
-  const bool dma = dma_offsets_fit(BM, p.lda, BK, p.ldb);
-  switch (path) {
-    case MfmaPath::Auto:
-      if (dma) return launch_dma_cfg<BM, BN, BK, DWM, DWN, true, 1, WIDE_ONLY>(p, va, vb, stream);
-      return launch_staged_cfg<BM, BN, BK, WM, WN, 4, kStoreGroup>(p, va, vb, stream);
-    case MfmaPath::Unpadded:
-      if (dma) return launch_dma_cfg<BM, BN, BK, DWM, DWN, false, 1, WIDE_ONLY>(p, va, vb, stream);
-      return launch_staged_cfg<BM, BN, BK, WM, WN, 0, kStoreGroup>(p, va, vb, stream);
-    case MfmaPath::Staged:
-      return launch_staged_cfg<BM, BN, BK, WM, WN, 4, kStoreGroup>(p, va, vb, stream);
+namespace {
+
+struct TileShape {
+  MfmaTile tile;
+  long bm, bn, threads;
+};
+
+// Largest first: the tie-break prefers the larger tile (fewer operand bytes
+// per flop, more L2 reuse).
+constexpr TileShape kTileShapes[] = {{MfmaTile::T256, 256, 256, 512},
+                                     {MfmaTile::T128, 128, 128, 512},
+                                     {MfmaTile::T64, 64, 64, 512},
+                                     {MfmaTile::T32x64, 32, 64, 256},
+                                     {MfmaTile::T32, 32, 32, 256}};
+
+// A launch's work-items (work-groups x threads) must fit 32 bits.
+constexpr double kMaxWorkItems = 4294967295.0;
+
+long tile_count(long M, long N, long bm, long bn, long batch) {
+  return ((M + bm - 1) / bm) * ((N + bn - 1) / bn) * batch;
+}
+
+// The share of the matrix-core time that a launch of this tile spends on
+// entries of C: every compute unit works through ceil(tiles / cus) tiles of
+// bm x bn, of which only M x N per product are wanted.  It is the product of
+// the round fill (tiles over rounds x CUs) and the area fill (M N over tiles
+// x bm bn); the rest is idle CUs in the last round and padding outside C.
+double tile_efficiency(const TileShape &t, long M, long N, int cus, long batch) {
+  const double tiles = (double)tile_count(M, N, t.bm, t.bn, batch);
+  if (tiles * t.threads > kMaxWorkItems) return 0.0;  // not launchable as one grid
+  const double rounds = ceil(tiles / cus);
+  return (double)M * N * batch / (rounds * cus * (double)t.bm * (double)t.bn);
+}
+
+// DMA configuration of a tile choice; wide: both operands take 16-byte loads
+// in the plain layout (the 256 x 256 tile exists only for that form).
+DmaCfg dma_cfg(TileChoice t, bool wide_plain) {
+  switch (t.tile) {
+    case MfmaTile::T256: return wide_plain ? DmaCfg::C256 : DmaCfg::C128;
+    case MfmaTile::T128: return DmaCfg::C128;
+    case MfmaTile::T64: return DmaCfg::C64;
+    case MfmaTile::T32x64: return t.long_k ? DmaCfg::C32x64L : DmaCfg::C32x64;
+    case MfmaTile::T32: return t.long_k ? DmaCfg::C32L : DmaCfg::C32;
   }
-  return hipErrorInvalidValue;
+  return DmaCfg::C128;
 }
 
-// The largest tile that still gives every compute unit a work-group and
-// whose tiles are at least 3/4 inside C (a 256 x 256 tile over a 64 x 64
-// product would compute 16 times the useful work); else 64 x 64, unless its
-// tiles would leave more than a quarter of the compute units idle: then the
-// k-split 32 x 32 tile.  (Four 32 x 32 work-groups per 64 x 64 tile; at 3/4
-// of the CUs or fewer they fit in three rounds where 64 x 64 needs one full
-// round each, and the measured crossover lies between 192 and 208 tiles on
-// 256 CUs.)
-MfmaTile choose_mfma_tile(long M, long N, int cus, long batch) {
-  auto tiles = [&](long t) { return (double)((M + t - 1) / t) * ((N + t - 1) / t) * batch; };
-  auto good = [&](long t) {
-    return tiles(t) >= cus && 4.0 * M * N * batch >= 3.0 * tiles(t) * t * t;
-  };
-  if (good(256)) return MfmaTile::T256;
-  if (good(128)) return MfmaTile::T128;
-  return 4.0 * tiles(64) <= 3.0 * cus ? MfmaTile::T32 : MfmaTile::T64;
+}  // namespace
+
+TileChoice with_slice_rule(MfmaTile tile, long M, long N, int cus, long batch) {
+  TileChoice c{tile, false};
+  for (const TileShape &t : kTileShapes)
+    if (t.tile == tile && (tile == MfmaTile::T32x64 || tile == MfmaTile::T32))
+      c.long_k = tile_count(M, N, t.bm, t.bn, batch) <= cus;
+  return c;
 }
 
-hipError_t launch_mfma(MfmaTile tile, MfmaPath path, const GemmArgs &p, bool va, bool vb,
+// Measured on 256 CUs (kernel trace and HIP events): 1000 x 1500 x 777
+// takes 32 x 64 (768 tiles, three full rounds: 31.9 -> 25.4 us against
+// 64 x 64, whose 384 tiles leave half the CUs idle in the second round);
+// 1024^3 takes 64 x 64 (256 tiles); 2048^3 128 x 128; 8192^3 256 x 256;
+// 256^3, 512^3 and 1000 x 130 x 2048 take 32 x 32.
+TileChoice choose_mfma_tile(long M, long N, int cus, long batch) {
+  double best = 0.0;
+  for (const TileShape &t : kTileShapes) best = fmax(best, tile_efficiency(t, M, N, cus, batch));
+  for (const TileShape &t : kTileShapes)
+    if (best > 0.0 && tile_efficiency(t, M, N, cus, batch) >= 0.97 * best)
+      return with_slice_rule(t.tile, M, N, cus, batch);
+  return with_slice_rule(MfmaTile::T128, M, N, cus, batch);
+}
+
+hipError_t launch_mfma(TileChoice tile, MfmaPath path, const GemmArgs &p, bool va, bool vb,
                        hipStream_t stream) {
-  switch (tile) {
-    case MfmaTile::T256:
-      // The 256 x 256 tile keeps 128 accumulators per lane; its 4-byte-load
-      // forms would spill, so operands that need them take the 128 x 128 tile.
-      if (!(va && vb)) return launch_tile<128, 128, 32, 2, 2, false, 4, 2>(path, p, va, vb, stream);
-      return launch_tile<256, 256, 32, 2, 4, true>(path, p, va, vb, stream);
-    case MfmaTile::T128:
-      return launch_tile<128, 128, 32, 2, 2, false, 4, 2>(path, p, va, vb, stream);
-    case MfmaTile::T64: return launch_tile<64, 64, 32, 2, 2>(path, p, va, vb, stream);
-    case MfmaTile::T32:
-      // The register-staged kernel has no k split: it takes the 64 x 64 tile.
-      if (path == MfmaPath::Staged || !dma_offsets_fit(32, p.lda, 32, p.ldb))
-        return launch_tile<64, 64, 32, 2, 2>(path, p, va, vb, stream);
-      if (path == MfmaPath::Unpadded)
-        return launch_dma_cfg<32, 32, 32, 1, 1, false, 1, false, 4>(p, va, vb, stream);
-      return launch_dma_cfg<32, 32, 32, 1, 1, true, 1, false, 4>(p, va, vb, stream);
-  }
-  return hipErrorInvalidValue;
+  if (path == MfmaPath::Staged) return launch_staged(tile.tile, true, p, va, vb, stream);
+  const DmaCfg c = dma_cfg(tile, va && vb);
+  const DmaGeom g = dma_geom(c);
+  // A slice whose offsets pass a buffer descriptor's 32-bit range takes the
+  // register-staged kernel (64-bit addressing).
+  if (!dma_offsets_fit(g.bm, p.lda, g.bk, p.ldb))
+    return launch_staged(tile.tile, path != MfmaPath::Unpadded, p, va, vb, stream);
+  if (path == MfmaPath::Unpadded) return launch_dma_layout<false, false, false>(c, p, va, vb, stream);
+  return launch_dma_layout<false, false, true>(c, p, va, vb, stream);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int KSPLIT = 1>
-static hipError_t launch_general_tile(const GemmArgs &p, bool ta, bool tb, bool va, bool vb,
-                                      hipStream_t stream) {
-  if (!dma_offsets_fit(ta ? BK : BM, p.lda, tb ? BN : BK, p.ldb)) return hipErrorInvalidValue;
-  return launch_dma_general<BM, BN, BK, WM, WN, KSPLIT>(p, ta, tb, va, vb, stream);
-}
-
-hipError_t launch_mfma_general(MfmaTile tile, const GemmArgs &p, bool ta, bool tb, bool va,
+hipError_t launch_mfma_general(TileChoice tile, const GemmArgs &p, bool ta, bool tb, bool va,
                                bool vb, hipStream_t stream) {
-  // The 256 x 256 tile is instantiated for the plain layout with 16-byte
-  // loads only (other forms would spill); the rest use 128 x 128.
-  if (tile == MfmaTile::T256 && !ta && !tb && va && vb) {
-    if (!dma_offsets_fit(256, p.lda, 32, p.ldb)) return hipErrorInvalidValue;
-    return launch_dma_cfg<256, 256, 32, 2, 4, true, 1, true>(p, va, vb, stream);
-  }
-  if (tile == MfmaTile::T64) return launch_general_tile<64, 64, 32, 2, 2>(p, ta, tb, va, vb, stream);
-  if (tile == MfmaTile::T32)
-    return launch_general_tile<32, 32, 32, 1, 1, 4>(p, ta, tb, va, vb, stream);
-  return launch_general_tile<128, 128, 32, 4, 2>(p, ta, tb, va, vb, stream);
+  const DmaCfg c = dma_cfg(tile, !ta && !tb && va && vb);
+  const DmaGeom g = dma_geom(c);
+  if (!dma_offsets_fit(ta ? g.bk : g.bm, p.lda, tb ? g.bn : g.bk, p.ldb))
+    return hipErrorInvalidValue;
+  if (!ta && !tb) return launch_dma_layout<false, false, true>(c, p, va, vb, stream);
+  if (!ta) return launch_dma_layout<false, true, true>(c, p, va, vb, stream);
+  if (!tb) return launch_dma_layout<true, false, true>(c, p, va, vb, stream);
+  return launch_dma_layout<true, true, true>(c, p, va, vb, stream);
 }
 
 // ---------------------------------------------------------------------------

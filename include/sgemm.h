@@ -42,9 +42,12 @@
  * before the library or the HIP runtime is consulted, so they are reported
  * even before sgemm_create.  sgemm_status_string() names each status.
  * Limits (SGEMM_ERR_TOO_LARGE): M, N, K and batch below 2^31, and one launch
- * below 2^32 work-items -- 256 per 64 x 64 block of C for the matrix-core
- * kernels (per 32 x 32 block for SGEMM_VARIANT_MFMA_32), 256 per 16 x 16
- * block for the vector-FMA variants.
+ * below 2^32 work-items.  sgemm_run and the general form take any product
+ * with at most 2^24 blocks of 64 x 64 (counting every product of a batch)
+ * and pick a tile whose launch fits; the forced tiles need 512 work-items
+ * per 64 x 64 block (SGEMM_VARIANT_MFMA_64) or 256 per 32 x 64
+ * (SGEMM_VARIANT_MFMA_32X64) or 32 x 32 block (SGEMM_VARIANT_MFMA_32), the
+ * vector-FMA variants 256 per 16 x 16 block.
  *
  * Threads.  sgemm_create / sgemm_destroy are serialised internally;
  * sgemm_run may be called from any thread once sgemm_create has succeeded.
@@ -77,12 +80,15 @@ extern "C" {
  * operand slices reach LDS by buffer-to-LDS loads, 16 bytes per lane where
  * the operand is 16-byte aligned with a leading dimension and width that are
  * multiples of 4, else 4 bytes; only an operand whose leading dimension puts
- * one slice beyond 2 GiB is fetched through registers instead.  The
- * _MFMA_<n> variants force its n x n block tile instead of choosing one
- * from the shape; the 32 x 32 tile (which sgemm_run picks when 64 x 64
- * tiles would fill at most 3/4 of the compute units) runs four waves on the same
- * block, each summing a quarter of every K slice, and adds their partial
- * sums in a fixed order.  SGEMM_VARIANT_MFMA_STAGED always fetches through
+ * one slice beyond 2 GiB is fetched through registers instead.  sgemm_run
+ * picks the block tile (256 x 256, 128 x 128, 64 x 64, 32 x 64 or 32 x 32)
+ * that loses the least matrix-core time to partly filled rounds of
+ * work-groups and to tile area outside C, the larger one when two come
+ * within 3%.  The _MFMA_<n> variants force a tile instead (with the same
+ * K-slice rule): the 64 x 64 tile runs two sets of four waves on the block,
+ * the 32 x 64 tile two sets of two and the 32 x 32 tile four single waves,
+ * each set summing its share of every K slice; the sets' partial sums are
+ * added in a fixed order.  SGEMM_VARIANT_MFMA_STAGED always fetches through
  * registers, SGEMM_VARIANT_MFMA_UNPADDED drops the LDS anti-conflict
  * layout (the chapter's padding, section 三), and SGEMM_VARIANT_MFMA_DWORD
  * fetches both operands 4 bytes per lane even where 16-byte loads are
@@ -102,7 +108,8 @@ extern "C" {
 #define SGEMM_VARIANT_MFMA_UNPADDED 9
 #define SGEMM_VARIANT_MFMA_32 10
 #define SGEMM_VARIANT_MFMA_DWORD 11
-#define SGEMM_NUM_VARIANTS 12
+#define SGEMM_VARIANT_MFMA_32X64 12
+#define SGEMM_NUM_VARIANTS 13
 
 /*
  * Initialise the library for the current device: checks that it is gfx950

@@ -82,17 +82,23 @@ def test_unknown_variant_rejected():
 
 
 def test_forced_tile_work_item_limits():
-    """A launch must stay below 2^32 work-items: 131072 x 131072 fits with
-    64 x 64 blocks (2^22 blocks x 256) but not with the forced 32 x 32 tile
-    (2^24 x 256); the checks come before anything touches the runtime."""
+    """A launch must stay below 2^32 work-items.  At 200000 x 200000 the
+    64 x 64 blocks number 3125^2: sgemm_run takes the product (it picks a
+    tile whose launch fits), but the forced 64 x 64 tile (512 per block),
+    32 x 64 and 32 x 32 tiles (256 per block) would not fit; at 131072^2 the
+    forced 64 x 64 tile does.  The checks come before anything touches the
+    runtime."""
     lib = sg.load_library()
-    n = 131072
-    rc = lib.sgemm_run_variant(sg.VARIANTS["mfma_32"], n, n, 1, 16, 1, 16, n, 16, n, None)
-    assert sg.sgemm_status_string(rc) == "SGEMM_ERR_TOO_LARGE"
-    rc = lib.sgemm_run_variant(sg.VARIANTS["mfma_64"], n, n, 1, 16, 1, 16, n, 16, n, None)
-    assert sg.sgemm_status_string(rc) == "SGEMM_ERR_NOT_INITIALIZED"
-    rc = lib.sgemm_run_variant(sg.VARIANTS["dbuf"], n, n, 1, 16, 1, 16, n, 16, n, None)
-    assert sg.sgemm_status_string(rc) == "SGEMM_ERR_TOO_LARGE"
+
+    def status(variant, n):
+        return sg.sgemm_status_string(
+            lib.sgemm_run_variant(sg.VARIANTS[variant], n, n, 1, 16, 1, 16, n, 16, n, None))
+
+    for v in ("mfma_64", "mfma_32x64", "mfma_32", "dbuf"):
+        assert status(v, 200000) == "SGEMM_ERR_TOO_LARGE", v
+    for v in ("mfma", "mfma_128", "mfma_256"):
+        assert status(v, 200000) == "SGEMM_ERR_NOT_INITIALIZED", v
+    assert status("mfma_64", 131072) == "SGEMM_ERR_NOT_INITIALIZED"
 
 
 def test_destroy_without_create():

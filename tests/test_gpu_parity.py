@@ -21,7 +21,7 @@ from dense_fp32_matrix_03_amd import inputs
 pytestmark = pytest.mark.gpu
 
 MFMA_VARIANTS = ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_staged", "mfma_unpadded",
-                 "mfma_32", "mfma_dword"]
+                 "mfma_32", "mfma_dword", "mfma_32x64"]
 VALU_VARIANTS = ["naive", "lds", "reg", "dbuf"]
 ALL_VARIANTS = VALU_VARIANTS + MFMA_VARIANTS
 
@@ -237,7 +237,8 @@ EXTREME_SHAPES = [(1, 1, 1 << 22), (2, 3, 1 << 20), (1 << 20, 3, 7), (5, 1 << 20
                   (4097, 4099, 1), (1 << 15, 1 << 9, 4)]
 
 
-@pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged", "mfma_32"])
+@pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged", "mfma_32",
+                                     "mfma_32x64"])
 @pytest.mark.parametrize("shape", EXTREME_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_extreme_aspect_ratios(variant, shape):
     M, N, K = shape
@@ -258,7 +259,7 @@ DMA_DIMS = [4, 8, 12, 28, 36, 60, 68, 124, 132, 252, 260, 516]
 
 
 @pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_unpadded",
-                                     "mfma_32", "mfma_dword"])
+                                     "mfma_32", "mfma_dword", "mfma_32x64"])
 def test_buffer_to_lds_edge_sweep(variant):
     g0 = np.random.default_rng(53 + MFMA_VARIANTS.index(variant))
     shapes = [tuple(int(x) for x in g0.choice(DMA_DIMS, 3)) for _ in range(20)]
@@ -276,23 +277,34 @@ def test_buffer_to_lds_edge_sweep(variant):
                                     (inputs.WORKLOADS[2], "mfma_128")],
                          ids=["1024", "2048"])
 def test_load_paths_agree_bitwise(w, tile):
-    """Buffer-to-LDS and register-staged fetches, with or without the LDS
-    anti-conflict layout, 16 or 4 bytes per lane, feed the same matrix-core
-    sequence: at the tile the shape selects they must give identical bits."""
+    """Buffer-to-LDS fetches with or without the LDS anti-conflict layout,
+    16 or 4 bytes per lane, feed the same matrix-core sequence: at the tile
+    the shape selects they give identical bits.  The register-staged kernel
+    has no k split, so it matches them at 128 x 128 (2048^3) and meets the
+    tolerance at 64 x 64, whose buffer-to-LDS form splits K over two sets of
+    waves (1024^3)."""
     import torch
     A, B = inputs.make_inputs(w)
     dA, dB = _dev(A), _dev(B)
-    outs = []
+    outs = {}
     for variant in ("mfma", tile, "mfma_staged", "mfma_unpadded", "mfma_dword"):
         dC = torch.full((w.M, w.N), float("nan"), dtype=torch.float32, device="cuda")
         sg.sgemm_run_variant(variant, w.M, w.N, w.K, dA, w.K, dB, w.N, dC, w.N)
         torch.cuda.synchronize()
-        outs.append(dC.cpu().numpy().tobytes())
-    assert all(o == outs[0] for o in outs[1:])
+        outs[variant] = dC.cpu().numpy()
+    same = ["mfma", tile, "mfma_unpadded", "mfma_dword"]
+    if tile == "mfma_128":
+        same.append("mfma_staged")
+    else:
+        Cref, Sabs = oracle.sgemm_f64(A, B)
+        r = oracle.check(outs["mfma_staged"], Cref, Sabs)
+        assert r.ok and r.usage < 0.05, str(r)
+    for v in same[1:]:
+        assert outs[v].tobytes() == outs["mfma"].tobytes(), v
 
 
 @pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged", "reg", "dbuf",
-                                     "mfma_32", "mfma_dword"])
+                                     "mfma_32", "mfma_dword", "mfma_32x64"])
 def test_padded_leading_dimensions(variant):
     """NaN in the padding of A and B must not reach C; C's padding is untouched."""
     M, N, K = 200, 136, 72
@@ -330,20 +342,53 @@ def test_misaligned_pointers(variant):
     assert r.ok, str(r)
 
 
+# sgemm_run's tile rule, restated: the tile that loses the least matrix-core
+# time to partly filled rounds of work-groups and to tile area outside C
+# (efficiency = M N batch / (rounds x CUs x tile area), rounds = ceil(tiles /
+# CUs)), the larger one when two come within 3%; a tile whose launch would
+# pass 2^32 work-items is out.
+TILE_RULE = [("mfma_256", 256, 256, 512), ("mfma_128", 128, 128, 512), ("mfma_64", 64, 64, 512),
+             ("mfma_32x64", 32, 64, 256), ("mfma_32", 32, 32, 256)]
+
+
+def _expected_tile(M, N, batch, cus):
+    def eff(bm, bn, threads):
+        tiles = -(-M // bm) * -(-N // bn) * batch
+        if tiles * threads > 2 ** 32 - 1:
+            return 0.0
+        rounds = -(-tiles // cus)
+        return float(M) * N * batch / (rounds * cus * bm * bn)
+    best = max(eff(bm, bn, t) for _, bm, bn, t in TILE_RULE)
+    for name, bm, bn, t in TILE_RULE:
+        if eff(bm, bn, t) >= 0.97 * best:
+            return name
+    return "mfma_128"
+
+
+def test_expected_tile_on_256_cus():
+    """The restated rule on 256 CUs picks the tiles measured best."""
+    assert _expected_tile(256, 256, 1, 256) == "mfma_32"
+    assert _expected_tile(512, 512, 1, 256) == "mfma_32"
+    assert _expected_tile(1000, 130, 1, 256) == "mfma_32"
+    assert _expected_tile(1000, 1500, 1, 256) == "mfma_32x64"
+    assert _expected_tile(1024, 1024, 1, 256) == "mfma_64"
+    assert _expected_tile(2048, 2048, 1, 256) == "mfma_128"
+    assert _expected_tile(8192, 8192, 1, 256) == "mfma_256"
+    assert _expected_tile(64, 64, 1024, 256) == "mfma_64"
+
+
 @pytest.mark.parametrize("M,N,K,batch", [
     (512, 512, 512, 1), (256, 256, 256, 1), (300, 260, 100, 1), (1000, 130, 2048, 1),
     (1024, 1024, 256, 1), (64, 64, 64, 256), (128, 128, 128, 8), (768, 1024, 512, 1),
-    (832, 1024, 512, 1)])
-def test_tile_choice_for_small_products(M, N, K, batch):
-    """Products whose 64 x 64 tiles (over the batch) would fill at most 3/4
-    of the compute units take the k-split 32 x 32 tile (on 256 CUs: 768 x
-    1024 with 192 tiles), the others keep 64 x 64 (832 x 1024: 208 tiles):
-    sgemm_run's bits equal those of the forced variant, and both meet the
-    oracle."""
+    (832, 1024, 512, 1), (1000, 1500, 776, 1), (640, 640, 2048, 1), (3072, 3072, 64, 1)])
+def test_tile_choice(M, N, K, batch):
+    """sgemm_run takes the tile of the rule above on this device's CU count:
+    its bits equal those of that forced tile (same K-slice rule), and both
+    meet the oracle.  A batch is checked against the oracle on its first and
+    last products."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    tiles64 = ((M + 63) // 64) * ((N + 63) // 64) * batch
-    tile = "mfma_32" if 4 * tiles64 <= 3 * cus else "mfma_64"
+    tile = _expected_tile(M, N, batch, cus)
     g = np.random.default_rng(M + N + K + batch)
     A = inputs.uniform(g, (batch, M, K))
     B = inputs.uniform(g, (batch, K, N))
@@ -354,7 +399,6 @@ def test_tile_choice_for_small_products(M, N, K, batch):
         if batch == 1:
             sg.sgemm_run_variant(variant, M, N, K, dA, K, dB, N, dC, N)
         else:
-            assert variant == "mfma"
             sg.sgemm_run_strided_batched(0, 0, M, N, K, 1.0, dA, K, M * K, dB, N, K * N, 0.0,
                                          dC, N, M * N, batch)
         torch.cuda.synchronize()
@@ -368,12 +412,6 @@ def test_tile_choice_for_small_products(M, N, K, batch):
         assert r.usage < 0.05
     if batch == 1:
         assert outs[0].tobytes() == outs[1].tobytes(), f"sgemm_run did not take {tile}"
-    else:
-        # One product of the batch through the forced tile gives the same bits.
-        dC1 = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
-        sg.sgemm_run_variant(tile, M, N, K, dA[0], K, dB[0], N, dC1, N)
-        torch.cuda.synchronize()
-        assert dC1.cpu().numpy().tobytes() == outs[0][0].tobytes(), f"batch did not take {tile}"
 
 
 def test_identity_gives_A_exactly():
