@@ -481,6 +481,80 @@ def kscan_table(variant, calls: int) -> list[dict]:
     return rows
 
 
+# Products whose phases --phases reports: the five workloads and the ends of
+# the K-scan.
+PHASE_SHAPES = ((256, 256, 256), (1024, 1024, 1024), (2048, 2048, 2048), (1000, 1500, 777),
+                (8192, 8192, 8192), (256, 256, 32), (256, 256, 4096), (1024, 1024, 32),
+                (1024, 1024, 4096))
+REALTIME_MHZ = 100.0  # s_memrealtime's reference clock on MI355X
+
+
+def phase_table(settle: float) -> list[dict]:
+    """Where a call's time goes: sgemm_phase_times on each PHASE_SHAPES
+    product (A row-major with lda = K unless the workload says otherwise),
+    after `settle` seconds of untimed calls, next to sgemm_run's own HIP-event
+    time per call.  Per work-group, from the timestamps of the last of 20
+    back-to-back calls: first-slice latency, main loop, k-set reduction,
+    stores; across work-groups the spread of their starts and the span from
+    the first start to the last end; the shader clock; and the main loop's
+    matrix-core time at that clock (64 cycles per 32x32x2 instruction)."""
+    import numpy as np
+    import torch
+
+    import dense_fp32_matrix_03_amd as sg
+    from dense_fp32_matrix_03_amd import inputs
+
+    rows = []
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    for M, N, K in PHASE_SHAPES:
+        lda = 777 if (M, N, K) == (1000, 1500, 777) else K
+        w = inputs.Workload(f"sgemm_{M}x{N}x{K}_uniform_seed{M + N + K}", M, N, K, "uniform",
+                            M + N + K, lda, N, N, "full")
+        ms, _ = time_gpu(w, sg.VARIANTS["mfma"], 20 if w.flops > 1e12 else 200, 5,
+                         warm_seconds=settle)
+        A, B = inputs.make_inputs(w)
+        dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        wgs = sg.sgemm_phase_times(M, N, K, dA, lda, dB, N, dC, N, None, 0, h)
+        t = torch.zeros(8 * wgs, dtype=torch.int64, device="cuda")
+        calls = 20
+        t_end = time.perf_counter() + settle
+        while True:
+            for _ in range(calls):
+                sg.sgemm_phase_times(M, N, K, dA, lda, dB, N, dC, N, t, t.numel(), h)
+            torch.cuda.synchronize()
+            if time.perf_counter() >= t_end:
+                break
+        q = t.cpu().numpy().astype(np.int64).reshape(wgs, 8)
+        tile = int(q[0, 7])
+        bm, bn, bk, ks = tile & 0xffff, (tile >> 16) & 0xffff, (tile >> 32) & 0xffff, tile >> 48
+        us = 1.0 / REALTIME_MHZ
+
+        def mean(a):
+            return float(np.mean(a)) * us
+
+        clock = float(np.mean((q[:, 6] - q[:, 5]) / np.maximum(q[:, 4] - q[:, 0], 1))) * REALTIME_MHZ
+        kp = -(-K // bk) * bk
+        mfma_per_simd = (bm // 32) * (bn // 32) * (kp // 2) / 4
+        loop_mfma_us = mfma_per_simd * 64 / clock
+        r = {"M": M, "N": N, "K": K, "lda": lda, "tile": f"{bm}x{bn}x{bk}", "k_sets": ks,
+             "workgroups": wgs, "call_us": round(ms * 1e3, 3),
+             "span_us": round(float(q[:, 4].max() - q[:, 0].min()) * us, 3),
+             "start_spread_us": round(float(q[:, 0].max() - q[:, 0].min()) * us, 3),
+             "first_slice_us": round(mean(q[:, 1] - q[:, 0]), 3),
+             "loop_us": round(mean(q[:, 2] - q[:, 1]), 3),
+             "reduce_us": round(mean(q[:, 3] - q[:, 2]), 3),
+             "store_us": round(mean(q[:, 4] - q[:, 3]), 3),
+             "workgroup_us": round(mean(q[:, 4] - q[:, 0]), 3),
+             "clock_mhz": round(clock, 0), "loop_mfma_us": round(loop_mfma_us, 3)}
+        print(json.dumps(r), flush=True)
+        rows.append(r)
+        del dA, dB, dC, t
+        torch.cuda.empty_cache()
+    return rows
+
+
 def _read_csv(path):
     import csv
     with open(path, newline="") as f:
@@ -773,6 +847,9 @@ def main(argv=None) -> int:
                     help="time sgemm_run at M = N = 256 and 1024 over K = 32 .. 4096, two "
                          "floor cases and the five workloads, one JSON line each (with the "
                          "dispatch range each case timed, for --trace-summary)")
+    ap.add_argument("--phases", action="store_true",
+                    help="where a call's time goes: per-work-group phase timestamps "
+                         "(sgemm_phase_times) on the workloads and the K-scan ends")
     ap.add_argument("--trace-summary", nargs="+", metavar=("TRACE_CSV", "CASES_JSONL"),
                     help="host only: summarise a rocprofv3 kernel trace (and optionally a "
                          "counter CSV) of a bench run per case: TRACE_CSV CASES_JSONL "
@@ -825,6 +902,10 @@ def main(argv=None) -> int:
         return 0
     if a.vector_add:
         vector_add_table(a.steps, a.settle)
+        sg.sgemm_destroy()
+        return 0
+    if a.phases:
+        phase_table(a.settle)
         sg.sgemm_destroy()
         return 0
     if a.kscan:

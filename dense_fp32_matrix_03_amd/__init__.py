@@ -85,6 +85,8 @@ def load_library(path: str = LIB_PATH):
     lib.vector_add.restype = ci
     lib.sgemm_mfma_ceiling.argtypes = [ci, ci, vp, i64, ctypes.POINTER(ctypes.c_double), vp]
     lib.sgemm_mfma_ceiling.restype = ci
+    lib.sgemm_phase_times.argtypes = gemm_args[:-1] + [vp, i64, ctypes.POINTER(i64), vp]
+    lib.sgemm_phase_times.restype = ci
     lib.sgemm_mfma_probe.argtypes = [ci, vp, vp, vp, vp]
     lib.sgemm_mfma_probe.restype = ci
     lib.sgemm_status_string.argtypes = [ci]
@@ -202,6 +204,16 @@ def sgemm_mfma_ceiling(which, iters, out, out_len, stream=None) -> float:
     _check("sgemm_mfma_ceiling", load_library().sgemm_mfma_ceiling(
         int(which), int(iters), _ptr(out), int(out_len), ctypes.byref(flops), _stream(stream)))
     return flops.value
+
+
+def sgemm_phase_times(M, N, K, A, lda, B, ldb, C, ldc, times, times_len, stream=None) -> int:
+    """sgemm_run with per-work-group phase timestamps in `times` (8 uint64
+    per work-group; times=None only queries); returns the work-group count."""
+    wgs = ctypes.c_int64(0)
+    _check("sgemm_phase_times", load_library().sgemm_phase_times(
+        M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(times), int(times_len),
+        ctypes.byref(wgs), _stream(stream)))
+    return wgs.value
 
 
 def sgemm_mfma_probe(which, A, B, C, stream=None) -> None:

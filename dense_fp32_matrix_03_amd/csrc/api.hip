@@ -155,10 +155,10 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
     const bool vb = aligned16(B) && ldb % 4 == 0 && N % 4 == 0;
     using sgemm::MfmaPath;
     using sgemm::MfmaTile;
-    const sgemm::TileChoice autotile = sgemm::choose_mfma_tile(M, N, di.cus);
+    const sgemm::TileChoice autotile = sgemm::choose_mfma_tile(M, N, K, di.cus);
     // A forced tile keeps the K-slice rule of the automatic choice, so it
     // gives sgemm_run's bits whenever sgemm_run picks the same tile.
-    auto forced = [&](MfmaTile t) { return sgemm::with_slice_rule(t, M, N, di.cus); };
+    auto forced = [&](MfmaTile t) { return sgemm::with_slice_rule(t, M, N, K, di.cus); };
     switch (variant) {
       case SGEMM_VARIANT_NAIVE:
       case SGEMM_VARIANT_LDS:
@@ -202,6 +202,40 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
 int sgemm_run(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
               int64_t ldb, float *C, int64_t ldc, void *stream) {
   return sgemm_run_variant(SGEMM_VARIANT_MFMA, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int sgemm_phase_times(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                      const float *B, int64_t ldb, float *C, int64_t ldc, uint64_t *times,
+                      int64_t times_len, int64_t *workgroups, void *stream) {
+  if (!workgroups || M < 1 || N < 1 || K < 1) return SGEMM_ERR_INVALID_VALUE;
+  int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc);
+  if (rc != SGEMM_OK) return rc;
+  if (!g_ready.load(std::memory_order_acquire)) return SGEMM_ERR_NOT_INITIALIZED;
+  DeviceInfo di;
+  rc = current_device_info(&di);
+  if (rc != SGEMM_OK) return rc;
+  sgemm::GemmArgs p;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.A = A;
+  p.lda = lda;
+  p.B = B;
+  p.ldb = ldb;
+  p.C = C;
+  p.ldc = ldc;
+  const bool va = aligned16(A) && lda % 4 == 0 && K % 4 == 0;
+  const bool vb = aligned16(B) && ldb % 4 == 0 && N % 4 == 0;
+  const sgemm::TileChoice tile = sgemm::choose_mfma_tile(M, N, K, di.cus);
+  long wgs = 0;
+  hipError_t err = sgemm::launch_mfma_phases(tile, p, va, vb, &wgs, nullptr);  // count only
+  if (err == hipErrorInvalidValue) return SGEMM_ERR_TOO_LARGE;
+  *workgroups = wgs;
+  if (times == nullptr) return SGEMM_OK;
+  if (times_len < 8 * (int64_t)wgs) return SGEMM_ERR_INVALID_VALUE;
+  p.phases = reinterpret_cast<unsigned long long *>(times);
+  err = sgemm::launch_mfma_phases(tile, p, va, vb, &wgs, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 
 int sgemm_run_strided_batched(int transA, int transB, int64_t M, int64_t N, int64_t K,
@@ -258,7 +292,7 @@ int sgemm_run_strided_batched(int transA, int transB, int64_t M, int64_t N, int6
     // dimensions, and a stored width that is a multiple of 4.
     const bool va = aligned16(A) && lda % 4 == 0 && strideA % 4 == 0 && a_cols % 4 == 0;
     const bool vb = aligned16(B) && ldb % 4 == 0 && strideB % 4 == 0 && b_cols % 4 == 0;
-    const sgemm::TileChoice tile = sgemm::choose_mfma_tile(M, N, di.cus, batch);
+    const sgemm::TileChoice tile = sgemm::choose_mfma_tile(M, N, K, di.cus, batch);
     err = sgemm::launch_mfma_general(tile, p, transA, transB, va, vb, s);
     if (err == hipErrorInvalidValue) return SGEMM_ERR_TOO_LARGE;
   }

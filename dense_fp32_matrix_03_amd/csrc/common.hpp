@@ -77,6 +77,8 @@ struct GemmArgs {
   float alpha = 1.f, beta = 0.f;
   long strideA = 0, strideB = 0, strideC = 0;
   int batch = 1;
+  // Phase timestamps (the diagnostic instantiation only): 8 per work-group.
+  unsigned long long *phases = nullptr;
 };
 
 // Register-staged fetch of a ROWS x COLS window (COLS a multiple of 4) of a

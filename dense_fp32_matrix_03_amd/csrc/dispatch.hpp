@@ -12,10 +12,13 @@ namespace sgemm {
 // 32 x 64 (two k sets) and 32 x 32 (four k sets).
 enum class MfmaTile { T256, T128, T64, T32x64, T32 };
 
-// A tile and its K-slice length: long_k selects 64-float slices, which the
-// four-wave tiles (32 x 64, 32 x 32) take when all their work-groups fit one
-// round on the compute units (no second work-group per CU hides the
-// per-slice barrier, and half as many slices halve its cost).
+// A tile and its K-slice length: long_k selects 64-float slices.  The
+// four-wave tiles (32 x 64, 32 x 32) take them when all their work-groups fit
+// one round on the compute units (no second work-group per CU hides the
+// per-slice barrier, and half as many slices halve its cost); the 64 x 64
+// tile, whose two k sets give each wave only half of every 32-float slice,
+// when K >= 2048 (1024 x 1024 x 2048: 38.7 -> 32.9 us; at K = 1024 the short
+// slices are 1% faster).
 struct TileChoice {
   MfmaTile tile;
   bool long_k;
@@ -34,10 +37,10 @@ enum class MfmaPath { Auto, Staged, Unpadded };
 // that wastes the least matrix-core time to partly filled rounds of
 // work-groups and to tile area outside C, preferring the larger tile when
 // two come within 3% of each other.
-TileChoice choose_mfma_tile(long M, long N, int cus, long batch = 1);
+TileChoice choose_mfma_tile(long M, long N, long K, int cus, long batch = 1);
 
 // `tile` with the K-slice length choose_mfma_tile would give it.
-TileChoice with_slice_rule(MfmaTile tile, long M, long N, int cus, long batch = 1);
+TileChoice with_slice_rule(MfmaTile tile, long M, long N, long K, int cus, long batch = 1);
 
 // Matrix-core product.  va / vb: A / B qualify for 128-bit loads.
 hipError_t launch_mfma(TileChoice tile, MfmaPath path, const GemmArgs &p, bool va, bool vb,
@@ -48,6 +51,13 @@ hipError_t launch_mfma(TileChoice tile, MfmaPath path, const GemmArgs &p, bool v
 // hipErrorInvalidValue if a slice's offsets do not fit a buffer descriptor.
 hipError_t launch_mfma_general(TileChoice tile, const GemmArgs &p, bool ta, bool tb, bool va,
                                bool vb, hipStream_t stream);
+
+// sgemm_run's buffer-to-LDS computation of the plain product with phase
+// timestamps in p.phases (8 per work-group); *workgroups receives the
+// launch's work-group count.  With p.phases null nothing is launched.
+// hipErrorInvalidValue if a slice's offsets do not fit a buffer descriptor.
+hipError_t launch_mfma_phases(TileChoice tile, const GemmArgs &p, bool va, bool vb,
+                              long *workgroups, hipStream_t stream);
 
 // Register-staged kernel (mfma_gemm.hpp) on a 256, 128 or 64 tile (others
 // take 64); padded = false drops its A row padding.

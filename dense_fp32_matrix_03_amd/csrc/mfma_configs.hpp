@@ -16,11 +16,12 @@ namespace sgemm {
 //   C256     256 x 256 x 32, 2 x 4 waves of 128 x 64 (plain layout, 16-byte loads)
 //   C128     128 x 128 x 32, 4 x 2 waves of  32 x 64
 //   C64       64 x  64 x 32, 2 x 2 waves of  32 x 32, two k sets (8 waves)
+//   C64L      the same with 64-float K slices
 //   C32x64    32 x  64 x 32, 1 x 2 waves of  32 x 32, two k sets (4 waves)
 //   C32x64L   the same with 64-float K slices
 //   C32       32 x  32 x 32, one wave, four k sets (4 waves)
 //   C32L      the same with 64-float K slices
-enum class DmaCfg { C256, C128, C64, C32x64, C32x64L, C32, C32L };
+enum class DmaCfg { C256, C128, C64, C64L, C32x64, C32x64L, C32, C32L };
 
 struct DmaGeom {
   int bm, bn, bk;
@@ -31,6 +32,7 @@ inline DmaGeom dma_geom(DmaCfg c) {
     case DmaCfg::C256: return {256, 256, 32};
     case DmaCfg::C128: return {128, 128, 32};
     case DmaCfg::C64: return {64, 64, 32};
+    case DmaCfg::C64L: return {64, 64, 64};
     case DmaCfg::C32x64: return {32, 64, 32};
     case DmaCfg::C32x64L: return {32, 64, 64};
     case DmaCfg::C32: return {32, 32, 32};
@@ -40,56 +42,70 @@ inline DmaGeom dma_geom(DmaCfg c) {
 }
 
 // Launch configuration c for operand layout (TA, TB); SWZ = false drops the
-// LDS swizzle.  C256 is instantiated only for the plain layout with 16-byte
-// loads on both operands (its other forms would spill); asked for anything
-// else it returns hipErrorInvalidValue.
-template <bool TA, bool TB, bool SWZ>
+// LDS swizzle; PHASES selects the diagnostic instantiation that writes
+// per-work-group timestamps to p.phases.  C256 is instantiated only for the
+// plain layout with 16-byte loads on both operands (its other forms would
+// spill); asked for anything else it returns hipErrorInvalidValue.
+template <bool TA, bool TB, bool SWZ, bool PHASES = false>
 hipError_t launch_dma_layout(DmaCfg c, const GemmArgs &p, bool va, bool vb, hipStream_t s);
 
-template <bool TA, bool TB, bool SWZ>
+template <bool TA, bool TB, bool SWZ, bool PHASES>
 hipError_t launch_dma_layout(DmaCfg c, const GemmArgs &p, bool va, bool vb, hipStream_t s) {
   constexpr int kGroupM = 8;  // tile rows per raster group
   switch (c) {
     case DmaCfg::C256:
       if constexpr (!TA && !TB) {
         if (!(va && vb)) return hipErrorInvalidValue;
-        launch_dma_kernel<256, 256, 32, 2, 4, SWZ, 1, true, true, false, false, 1, 2>(p, s,
-                                                                                     kGroupM);
+        launch_dma_kernel<256, 256, 32, 2, 4, SWZ, 1, true, true, false, false, 1, 2, PHASES>(
+            p, s, kGroupM);
         return hipGetLastError();
       }
       return hipErrorInvalidValue;
     case DmaCfg::C128:
-      launch_dma_widths<128, 128, 32, 4, 2, SWZ, 1, TA, TB, 1, 2>(p, va, vb, s, kGroupM);
+      launch_dma_widths<128, 128, 32, 4, 2, SWZ, 1, TA, TB, 1, 2,
+                        PHASES>(p, va, vb, s, kGroupM);
       break;
     case DmaCfg::C64:
-      launch_dma_widths<64, 64, 32, 2, 2, SWZ, 1, TA, TB, 2, 2>(p, va, vb, s, kGroupM);
+      launch_dma_widths<64, 64, 32, 2, 2, SWZ, 1, TA, TB, 2, 2,
+                        PHASES>(p, va, vb, s, kGroupM);
+      break;
+    case DmaCfg::C64L:
+      launch_dma_widths<64, 64, 64, 2, 2, SWZ, 1, TA, TB, 2, 2,
+                        PHASES>(p, va, vb, s, kGroupM);
       break;
     case DmaCfg::C32x64:
-      launch_dma_widths<32, 64, 32, 1, 2, SWZ, 1, TA, TB, 2, 2>(p, va, vb, s, kGroupM);
+      launch_dma_widths<32, 64, 32, 1, 2, SWZ, 1, TA, TB, 2, 2,
+                        PHASES>(p, va, vb, s, kGroupM);
       break;
     case DmaCfg::C32x64L:
-      launch_dma_widths<32, 64, 64, 1, 2, SWZ, 1, TA, TB, 2, 2>(p, va, vb, s, kGroupM);
+      launch_dma_widths<32, 64, 64, 1, 2, SWZ, 1, TA, TB, 2, 2,
+                        PHASES>(p, va, vb, s, kGroupM);
       break;
     case DmaCfg::C32:
-      launch_dma_widths<32, 32, 32, 1, 1, SWZ, 1, TA, TB, 4, 2>(p, va, vb, s, kGroupM);
+      launch_dma_widths<32, 32, 32, 1, 1, SWZ, 1, TA, TB, 4, 2,
+                        PHASES>(p, va, vb, s, kGroupM);
       break;
     case DmaCfg::C32L:
-      launch_dma_widths<32, 32, 64, 1, 1, SWZ, 1, TA, TB, 4, 2>(p, va, vb, s, kGroupM);
+      launch_dma_widths<32, 32, 64, 1, 1, SWZ, 1, TA, TB, 4, 2,
+                        PHASES>(p, va, vb, s, kGroupM);
       break;
   }
   return hipGetLastError();
 }
 
 // Instantiated in mfma_layout_*.hip.
-extern template hipError_t launch_dma_layout<false, false, true>(DmaCfg, const GemmArgs &, bool,
-                                                                 bool, hipStream_t);
-extern template hipError_t launch_dma_layout<false, false, false>(DmaCfg, const GemmArgs &, bool,
-                                                                  bool, hipStream_t);
-extern template hipError_t launch_dma_layout<false, true, true>(DmaCfg, const GemmArgs &, bool,
-                                                                bool, hipStream_t);
-extern template hipError_t launch_dma_layout<true, false, true>(DmaCfg, const GemmArgs &, bool,
-                                                                bool, hipStream_t);
-extern template hipError_t launch_dma_layout<true, true, true>(DmaCfg, const GemmArgs &, bool,
-                                                               bool, hipStream_t);
+extern template hipError_t launch_dma_layout<false, false, true, false>(DmaCfg, const GemmArgs &,
+                                                                        bool, bool, hipStream_t);
+extern template hipError_t launch_dma_layout<false, false, false, false>(DmaCfg,
+                                                                         const GemmArgs &, bool,
+                                                                         bool, hipStream_t);
+extern template hipError_t launch_dma_layout<false, true, true, false>(DmaCfg, const GemmArgs &,
+                                                                       bool, bool, hipStream_t);
+extern template hipError_t launch_dma_layout<true, false, true, false>(DmaCfg, const GemmArgs &,
+                                                                       bool, bool, hipStream_t);
+extern template hipError_t launch_dma_layout<true, true, true, false>(DmaCfg, const GemmArgs &,
+                                                                      bool, bool, hipStream_t);
+extern template hipError_t launch_dma_layout<false, false, true, true>(DmaCfg, const GemmArgs &,
+                                                                       bool, bool, hipStream_t);
 
 }  // namespace sgemm

@@ -168,10 +168,33 @@ struct SliceGeom {
 // that ends slice t, into the stage slice t has released, and the barrier
 // that ends slice t+1 waits only for slice t+1 -- NST-1 slices of latency
 // cover.  When K fits NST slices, every slice is in flight from the start.
+//
+// PHASES (a diagnostic instantiation): thread 0 of each work-group writes
+// the reference-clock time (s_memrealtime) at five points of its run to
+// p.phases[8 w + i] -- 0 start, 1 first slice landed, 2 last slice
+// computed, 3 k-set sums reduced, 4 stores of C complete -- the shader
+// clock (s_memtime) at start and end to entries 5 and 6, and the tile (BM,
+// BN, BK, KSPLIT in 16-bit fields) to entry 7.  The only other change is a
+// wait for the stores before the last timestamp, which the product kernel
+// leaves to the end of the dispatch.
 template <int BM, int BN, int BK, int WM, int WN, bool SWZ, bool KFULL, int SCHED, bool VA,
-          bool VB, bool TA, bool TB, int KSPLIT = 1, int NST = 2>
+          bool VB, bool TA, bool TB, int KSPLIT = 1, int NST = 2, bool PHASES = false>
 __global__ void __launch_bounds__(WM *WN *KSPLIT *kWave)
 mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
+  auto phase = [&](int i) {
+    if constexpr (PHASES) {
+      if (threadIdx.x == 0) p.phases[(long)blockIdx.x * 8 + i] = __builtin_amdgcn_s_memrealtime();
+    }
+  };
+  phase(0);
+  if constexpr (PHASES) {
+    if (threadIdx.x == 0) {
+      p.phases[(long)blockIdx.x * 8 + 5] = __builtin_amdgcn_s_memtime();
+      p.phases[(long)blockIdx.x * 8 + 7] = (unsigned long long)BM | (unsigned long long)BN << 16 |
+                                           (unsigned long long)BK << 32 |
+                                           (unsigned long long)KSPLIT << 48;
+    }
+  }
   constexpr int NWT = WM * WN;       // waves of one k set
   constexpr int NW = NWT * KSPLIT;   // waves of the work-group
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -407,6 +430,7 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   static_for<NST>([&](auto S) { dma(S, decltype(S)::value); });
   // Slice 0 has landed; slices 1 .. NST-1 may still fly.
   dma_barrier_keep<(NST - 1) * kLoadsPerSlice>();
+  phase(1);
   read_ops(S0(), 0, cur);
   for (int t = 0; t < nk; t += NST) {
     static_for<NST>([&](auto S) {
@@ -416,6 +440,7 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   // The last slices issued loads past K (zero-filling, no memory traffic);
   // let them retire before the work-group gives up its LDS.
   __builtin_amdgcn_s_waitcnt(0x0f70);
+  phase(2);
 
   if constexpr (KSPLIT > 1) {
     // k sets 1.. leave their sums in LDS; set 0 adds them in order and
@@ -443,6 +468,7 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
             acc[i][j][e] += Red[(q - 1) * kRedSlot + (((wl * FM + i) * FN + j) * 16 + e) * kWave + lane];
   }
 
+  phase(3);
   // Epilogue: register e of lane l holds row acc32_row(l, e), column l % 32
   // of its 32x32 block; rows >= M and columns >= N are not stored.  C is read
   // only when beta != 0, and then a block's 16 values per lane are all loaded
@@ -479,76 +505,45 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
           if (inside(e)) *at(e) = fmaf(p.alpha, acc[i][j][e], p.beta * c[e]);
       }
     }
+  if constexpr (PHASES) {
+    __builtin_amdgcn_s_waitcnt(0);
+    phase(4);
+    if (threadIdx.x == 0) p.phases[(long)blockIdx.x * 8 + 6] = __builtin_amdgcn_s_memtime();
+  }
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool SWZ, int SCHED, bool VA, bool VB, bool TA,
-          bool TB, int KSPLIT, int NST>
+          bool TB, int KSPLIT, int NST, bool PHASES = false>
 inline void launch_dma_kernel(const GemmArgs &p, hipStream_t stream, int group_m) {
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const dim3 grid((unsigned)((long)tiles_m * tiles_n * p.batch)),
       block(WM * WN * KSPLIT * kWave);
   if (p.K % BK == 0)
-    hipLaunchKernelGGL(
-        (mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, true, SCHED, VA, VB, TA, TB, KSPLIT, NST>),
-        grid, block, 0, stream, p, tiles_m, tiles_n, group_m);
+    hipLaunchKernelGGL((mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, true, SCHED, VA, VB, TA, TB,
+                                             KSPLIT, NST, PHASES>),
+                       grid, block, 0, stream, p, tiles_m, tiles_n, group_m);
   else
-    hipLaunchKernelGGL(
-        (mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, false, SCHED, VA, VB, TA, TB, KSPLIT, NST>),
-        grid, block, 0, stream, p, tiles_m, tiles_n, group_m);
+    hipLaunchKernelGGL((mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, false, SCHED, VA, VB, TA,
+                                             TB, KSPLIT, NST, PHASES>),
+                       grid, block, 0, stream, p, tiles_m, tiles_n, group_m);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool SWZ, int SCHED, bool TA, bool TB,
-          int KSPLIT, int NST>
+          int KSPLIT, int NST, bool PHASES = false>
 inline void launch_dma_widths(const GemmArgs &p, bool va, bool vb, hipStream_t stream,
                               int group_m) {
   if (va && vb)
-    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true, TA, TB, KSPLIT, NST>(
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true, TA, TB, KSPLIT, NST, PHASES>(
         p, stream, group_m);
   else if (va)
-    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, false, TA, TB, KSPLIT, NST>(
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, false, TA, TB, KSPLIT, NST, PHASES>(
         p, stream, group_m);
   else if (vb)
-    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, true, TA, TB, KSPLIT, NST>(
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, true, TA, TB, KSPLIT, NST, PHASES>(
         p, stream, group_m);
   else
-    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, false, TA, TB, KSPLIT, NST>(
+    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, false, false, TA, TB, KSPLIT, NST, PHASES>(
         p, stream, group_m);
-}
-
-// Plain layout (no transposes).  WIDE_ONLY instantiates only the 16-byte-load
-// form; the caller guarantees va && vb.
-template <int BM, int BN, int BK, int WM, int WN, bool SWZ = true, int SCHED = 1,
-          bool WIDE_ONLY = false, int KSPLIT = 1, int NST = 2>
-inline hipError_t launch_dma_cfg(const GemmArgs &p, bool va, bool vb, hipStream_t stream,
-                                 int group_m = 8) {
-  if constexpr (WIDE_ONLY) {
-    if (!(va && vb)) return hipErrorInvalidValue;
-    launch_dma_kernel<BM, BN, BK, WM, WN, SWZ, SCHED, true, true, false, false, KSPLIT, NST>(
-        p, stream, group_m);
-  } else {
-    launch_dma_widths<BM, BN, BK, WM, WN, SWZ, SCHED, false, false, KSPLIT, NST>(p, va, vb,
-                                                                                 stream, group_m);
-  }
-  return hipGetLastError();
-}
-
-// Any layout.
-template <int BM, int BN, int BK, int WM, int WN, int KSPLIT = 1, int NST = 2>
-inline hipError_t launch_dma_general(const GemmArgs &p, bool ta, bool tb, bool va, bool vb,
-                                     hipStream_t stream, int group_m = 8) {
-  if (!ta && !tb)
-    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, false, false, KSPLIT, NST>(p, va, vb, stream,
-                                                                              group_m);
-  else if (!ta)
-    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, false, true, KSPLIT, NST>(p, va, vb, stream,
-                                                                             group_m);
-  else if (!tb)
-    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, true, false, KSPLIT, NST>(p, va, vb, stream,
-                                                                             group_m);
-  else
-    launch_dma_widths<BM, BN, BK, WM, WN, true, 1, true, true, KSPLIT, NST>(p, va, vb, stream,
-                                                                            group_m);
-  return hipGetLastError();
 }
 
 }  // namespace sgemm

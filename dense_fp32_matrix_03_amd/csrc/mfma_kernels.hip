@@ -50,7 +50,7 @@ DmaCfg dma_cfg(TileChoice t, bool wide_plain) {
   switch (t.tile) {
     case MfmaTile::T256: return wide_plain ? DmaCfg::C256 : DmaCfg::C128;
     case MfmaTile::T128: return DmaCfg::C128;
-    case MfmaTile::T64: return DmaCfg::C64;
+    case MfmaTile::T64: return t.long_k ? DmaCfg::C64L : DmaCfg::C64;
     case MfmaTile::T32x64: return t.long_k ? DmaCfg::C32x64L : DmaCfg::C32x64;
     case MfmaTile::T32: return t.long_k ? DmaCfg::C32L : DmaCfg::C32;
   }
@@ -59,8 +59,9 @@ DmaCfg dma_cfg(TileChoice t, bool wide_plain) {
 
 }  // namespace
 
-TileChoice with_slice_rule(MfmaTile tile, long M, long N, int cus, long batch) {
+TileChoice with_slice_rule(MfmaTile tile, long M, long N, long K, int cus, long batch) {
   TileChoice c{tile, false};
+  if (tile == MfmaTile::T64) c.long_k = K >= 2048;
   for (const TileShape &t : kTileShapes)
     if (t.tile == tile && (tile == MfmaTile::T32x64 || tile == MfmaTile::T32))
       c.long_k = tile_count(M, N, t.bm, t.bn, batch) <= cus;
@@ -72,13 +73,13 @@ TileChoice with_slice_rule(MfmaTile tile, long M, long N, int cus, long batch) {
 // 64 x 64, whose 384 tiles leave half the CUs idle in the second round);
 // 1024^3 takes 64 x 64 (256 tiles); 2048^3 128 x 128; 8192^3 256 x 256;
 // 256^3, 512^3 and 1000 x 130 x 2048 take 32 x 32.
-TileChoice choose_mfma_tile(long M, long N, int cus, long batch) {
+TileChoice choose_mfma_tile(long M, long N, long K, int cus, long batch) {
   double best = 0.0;
   for (const TileShape &t : kTileShapes) best = fmax(best, tile_efficiency(t, M, N, cus, batch));
   for (const TileShape &t : kTileShapes)
     if (best > 0.0 && tile_efficiency(t, M, N, cus, batch) >= 0.97 * best)
-      return with_slice_rule(t.tile, M, N, cus, batch);
-  return with_slice_rule(MfmaTile::T128, M, N, cus, batch);
+      return with_slice_rule(t.tile, M, N, K, cus, batch);
+  return with_slice_rule(MfmaTile::T128, M, N, K, cus, batch);
 }
 
 hipError_t launch_mfma(TileChoice tile, MfmaPath path, const GemmArgs &p, bool va, bool vb,
@@ -92,6 +93,16 @@ hipError_t launch_mfma(TileChoice tile, MfmaPath path, const GemmArgs &p, bool v
     return launch_staged(tile.tile, path != MfmaPath::Unpadded, p, va, vb, stream);
   if (path == MfmaPath::Unpadded) return launch_dma_layout<false, false, false>(c, p, va, vb, stream);
   return launch_dma_layout<false, false, true>(c, p, va, vb, stream);
+}
+
+hipError_t launch_mfma_phases(TileChoice tile, const GemmArgs &p, bool va, bool vb,
+                              long *workgroups, hipStream_t stream) {
+  const DmaCfg c = dma_cfg(tile, va && vb);
+  const DmaGeom g = dma_geom(c);
+  if (!dma_offsets_fit(g.bm, p.lda, g.bk, p.ldb)) return hipErrorInvalidValue;
+  *workgroups = (long)((p.M + g.bm - 1) / g.bm) * ((p.N + g.bn - 1) / g.bn);
+  if (p.phases == nullptr) return hipSuccess;
+  return launch_dma_layout<false, false, true, true>(c, p, va, vb, stream);
 }
 
 hipError_t launch_mfma_general(TileChoice tile, const GemmArgs &p, bool ta, bool tb, bool va,

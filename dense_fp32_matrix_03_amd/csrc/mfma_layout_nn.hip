@@ -3,6 +3,6 @@
 #include "mfma_configs.hpp"
 
 namespace sgemm {
-template hipError_t launch_dma_layout<false, false, true>(DmaCfg, const GemmArgs &, bool, bool,
+template hipError_t launch_dma_layout<false, false, true, false>(DmaCfg, const GemmArgs &, bool, bool,
                                                      hipStream_t);
 }  // namespace sgemm

@@ -210,6 +210,37 @@ int sgemm_mfma_probe(int which, const float *A, const float *B, float *C, void *
 int sgemm_mfma_ceiling(int which, int iters, float *out, int64_t out_len, double *flops,
                        void *stream);
 
+/*
+ * Diagnostic: sgemm_run's computation of C = A x B (the same tile choice,
+ * kernel code and result bits, for operands that take the buffer-to-LDS
+ * path) with timestamps that show where a call's time goes.  Thread 0 of
+ * each work-group w records, in the device buffer `times`, times[8w + i] for
+ *   i = 0  start of the work-group,
+ *       1  its first K slice has landed in LDS (the first load's latency),
+ *       2  its last slice is computed (the main loop),
+ *       3  the partial sums of its k sets are added (tiles that split K),
+ *       4  its stores of C are complete,
+ * on the device's constant reference clock (s_memrealtime, 100 MHz on
+ * MI355X), its shader clock (s_memtime, in cycles) at the start and at the
+ * end in times[8w + 5] and times[8w + 6], and its tile in times[8w + 7]:
+ * BM | BN << 16 | BK << 32 | KSPLIT << 48 (block rows and columns, K-slice
+ * length, k sets).  Waiting for the stores before
+ * the last timestamp is the only difference from sgemm_run's kernel, which
+ * leaves that wait to the end of the dispatch.  These are the pipeline
+ * stages of the textbook chapter "4. 矩阵乘法性能优化" (sections 一 to 四) and
+ * the measurement its section 五 asks for.
+ *
+ * *workgroups (host) receives the work-group count; with times == NULL
+ * nothing is launched (a size query).  M, N and K must be at least 1
+ * (SGEMM_ERR_INVALID_VALUE); times_len < 8 * *workgroups is
+ * SGEMM_ERR_INVALID_VALUE; SGEMM_ERR_TOO_LARGE where sgemm_run would fetch
+ * through registers (a leading dimension that puts one K slice beyond 2 GiB).
+ * Other checks and statuses as for sgemm_run.
+ */
+int sgemm_phase_times(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                      const float *B, int64_t ldb, float *C, int64_t ldc, uint64_t *times,
+                      int64_t times_len, int64_t *workgroups, void *stream);
+
 /* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
 const char *sgemm_status_string(int status);
 

@@ -451,6 +451,40 @@ def test_deterministic_bits_k_split_tile(M, N, K):
     assert not np.isnan(np.frombuffer(outs[0], dtype=np.float32)).any()
 
 
+# -- the phase-timestamp diagnostic ----------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,lda", [(256, 256, 256, 256), (1000, 1500, 777, 777),
+                                       (1024, 1024, 2048, 2048), (2048, 2048, 96, 96)])
+def test_phase_times_diagnostic(M, N, K, lda):
+    """sgemm_phase_times computes sgemm_run's bits (same tile and kernel
+    code), and each work-group's timestamps are in order (start <= first
+    slice landed <= last slice computed <= k sets reduced <= stores
+    complete), with a tile record whose block count matches the launch."""
+    import torch
+    g = np.random.default_rng(M + N + K)
+    A = inputs.padded(inputs.uniform(g, (M, K)), lda)
+    B = inputs.uniform(g, (K, N))
+    dA, dB = _dev(A), _dev(B)
+    dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    dR = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    wgs = sg.sgemm_phase_times(M, N, K, dA, lda, dB, N, dC, N, None, 0)
+    assert wgs > 0
+    t = torch.zeros(8 * wgs, dtype=torch.int64, device="cuda")
+    with pytest.raises(sg.SgemmError):
+        sg.sgemm_phase_times(M, N, K, dA, lda, dB, N, dC, N, t, t.numel() - 1)
+    assert sg.sgemm_phase_times(M, N, K, dA, lda, dB, N, dC, N, t, t.numel()) == wgs
+    sg.sgemm_run(M, N, K, dA, lda, dB, N, dR, N)
+    torch.cuda.synchronize()
+    assert dC.cpu().numpy().tobytes() == dR.cpu().numpy().tobytes()
+    q = t.cpu().numpy().reshape(wgs, 8)
+    assert np.all(np.diff(q[:, :5], axis=1) >= 0), "phase timestamps out of order"
+    assert np.all(q[:, 6] > q[:, 5]), "shader clock did not advance"
+    tile = int(q[0, 7])
+    assert np.all(q[:, 7] == tile)
+    bm, bn, bk, ks = tile & 0xffff, (tile >> 16) & 0xffff, (tile >> 32) & 0xffff, tile >> 48
+    assert -(-M // bm) * -(-N // bn) == wgs and bk in (32, 64) and ks in (1, 2, 4)
+
+
 # -- degenerate sizes and errors --------------------------------------------------------
 
 def test_k_zero_writes_zeros():
