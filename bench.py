@@ -47,8 +47,10 @@ COPY_BYTES = 256 << 20  # bytes read (and written) by the copy-calibration kerne
 
 
 # Sources that define the kernel sgemm_run launches for aligned operands (its
-# template, its shared helpers and the file that picks its configuration).
-HOT_KERNEL_SOURCES = ("common.hpp", "mfma_dma.hpp", "mfma_kernels.hip")
+# template, its shared helpers, its configurations, the file that
+# instantiates them and the one that picks the configuration).
+HOT_KERNEL_SOURCES = ("common.hpp", "mfma_dma.hpp", "mfma_configs.hpp", "mfma_layout_nn.hip",
+                      "mfma_kernels.hip")
 
 
 def kernel_source_digest() -> str:
@@ -85,6 +87,60 @@ LAST_TIMED = [(0, 0)]
 def trace_fields() -> dict:
     first, n = LAST_TIMED[0]
     return {"trace_first": first, "trace_calls": n}
+
+
+def write_hbm_counters(fetch_csv: str, write_csv: str, copy_fetch_csv: str,
+                       copy_write_csv: str, out: str = COUNTERS) -> dict:
+    """Host only: turn four rocprofv3 counter CSVs into the HBM-traffic
+    summary the headline line quotes.  FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) of the product kernel's dispatches in a run of the headline
+    command, each scaled by what the same counter reads for the runtime's
+    256 MiB device copy (COPY_BYTES read and written, from a run of
+    --copy-calibration): scale = COPY_BYTES / (KiB x 1024).  Stamped with the
+    digest of the hot kernel's sources."""
+    import csv
+
+    def values(path, counter, kernel):
+        with open(path, newline="") as f:
+            return [float(r["Counter_Value"]) for r in csv.DictReader(f)
+                    if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
+
+    fetch = values(fetch_csv, "FETCH_SIZE", "mfma_gemm_dma_kernel")
+    write = values(write_csv, "WRITE_SIZE", "mfma_gemm_dma_kernel")
+    cfetch = values(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
+    cwrite = values(copy_write_csv, "WRITE_SIZE", "copyBuffer")
+    if not (fetch and write and cfetch and cwrite):
+        raise ValueError("a counter CSV holds no dispatch of the expected kernel")
+    with open(fetch_csv, newline="") as f:
+        kernel = next(r["Kernel_Name"] for r in csv.DictReader(f)
+                      if "mfma_gemm_dma_kernel" in r["Kernel_Name"])
+    fscale = COPY_BYTES / (sum(cfetch) / len(cfetch) * 1024)
+    wscale = COPY_BYTES / (sum(cwrite) / len(cwrite) * 1024)
+    hbm = (sum(fetch) / len(fetch) * fscale + sum(write) / len(write) * wscale) * 1024
+    from dense_fp32_matrix_03_amd import inputs
+    cmd = "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {} --output-format csv -d <out> -o run -- "
+    c = {"kernel": kernel, "workload": HEADLINE,
+         "commands": {"FETCH_SIZE": cmd.format("FETCH_SIZE") + "python3 <repo>/bench.py "
+                      "--steps 3 --warmup 1 --no-cpu-baseline --no-secondary",
+                      "WRITE_SIZE": cmd.format("WRITE_SIZE") + "python3 <repo>/bench.py "
+                      "--steps 3 --warmup 1 --no-cpu-baseline --no-secondary",
+                      "copy_FETCH_SIZE": cmd.format("FETCH_SIZE") + "python3 <repo>/bench.py "
+                      "--copy-calibration",
+                      "copy_WRITE_SIZE": cmd.format("WRITE_SIZE") + "python3 <repo>/bench.py "
+                      "--copy-calibration",
+                      "summary": "python3 bench.py --write-hbm-counters FETCH WRITE COPY_FETCH "
+                                 "COPY_WRITE (run_counter_collection.csv of each)"},
+         "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+         "copy_kernel": "__amd_rocclr_copyBuffer, 256 MiB read + 256 MiB written",
+         "copy_fetch_kib_per_dispatch": cfetch, "copy_write_kib_per_dispatch": cwrite,
+         "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4),
+         "hbm_bytes_per_launch": int(round(hbm)),
+         "algorithmic_bytes_per_launch": inputs.BY_NAME[HEADLINE].min_bytes,
+         "source_files": list(HOT_KERNEL_SOURCES), "source_sha256": kernel_source_digest()}
+    with open(out, "w") as f:
+        json.dump(c, f, indent=1)
+        f.write("\n")
+    return c
 
 
 def time_gpu(w, variant: str, steps: int, warmup: int, warm_seconds: float = 0.0,
@@ -854,11 +910,20 @@ def main(argv=None) -> int:
                     help="host only: summarise a rocprofv3 kernel trace (and optionally a "
                          "counter CSV) of a bench run per case: TRACE_CSV CASES_JSONL "
                          "[COUNTERS_CSV]")
+    ap.add_argument("--write-hbm-counters", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="host only: write the HBM-traffic summary of the headline kernel "
+                         "from four rocprofv3 counter CSVs (see profiles/)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     a = ap.parse_args(argv)
 
+    if a.write_hbm_counters:
+        c = write_hbm_counters(*a.write_hbm_counters)
+        print(json.dumps({k: c[k] for k in ("hbm_bytes_per_launch", "fetch_scale",
+                                            "write_scale")}))
+        return 0
     if a.trace_summary:
         if len(a.trace_summary) not in (2, 3):
             ap.error("--trace-summary takes TRACE_CSV CASES_JSONL [COUNTERS_CSV]")

@@ -476,7 +476,7 @@ const char *sgemm_variant_name(int variant) {
     case SGEMM_VARIANT_MFMA: return "mfma_auto";
     case SGEMM_VARIANT_MFMA_256: return "mfma_256x256";
     case SGEMM_VARIANT_MFMA_128: return "mfma_128x128";
-    case SGEMM_VARIANT_MFMA_64: return "mfma_64x64_ksplit2";
+    case SGEMM_VARIANT_MFMA_64: return "mfma_64x64";
     case SGEMM_VARIANT_MFMA_32: return "mfma_32x32_ksplit4";
     case SGEMM_VARIANT_MFMA_STAGED: return "mfma_register_staged";
     case SGEMM_VARIANT_MFMA_UNPADDED: return "mfma_unpadded_lds";

@@ -8,20 +8,27 @@
 namespace sgemm {
 
 // Block tiles of the matrix-core kernels (mfma_configs.hpp gives their wave
-// grids): 256 x 256, 128 x 128, 64 x 64 (K split over two sets of waves),
-// 32 x 64 (two k sets) and 32 x 32 (four k sets).
+// grids): 256 x 256, 128 x 128, 64 x 64, 32 x 64 (K split over two sets of
+// waves) and 32 x 32 (four k sets).
 enum class MfmaTile { T256, T128, T64, T32x64, T32 };
 
-// A tile and its K-slice length: long_k selects 64-float slices.  The
-// four-wave tiles (32 x 64, 32 x 32) take them when all their work-groups fit
-// one round on the compute units (no second work-group per CU hides the
-// per-slice barrier, and half as many slices halve its cost); the 64 x 64
-// tile, whose two k sets give each wave only half of every 32-float slice,
-// when K >= 2048 (1024 x 1024 x 2048: 38.7 -> 32.9 us; at K = 1024 the short
-// slices are 1% faster).
+// A tile and its form.  long_k selects 64-float K slices; ksplit (64 x 64
+// only) runs the tile with two k sets of four waves.
+//  - The four-wave tiles (32 x 64, 32 x 32) take 64-float slices when all
+//    their work-groups fit one round on the compute units: no second
+//    work-group per CU hides the per-slice barrier, and half as many slices
+//    halve its cost.
+//  - The 64 x 64 tile takes two k sets (8 waves) when its work-groups fit
+//    one round and K >= 512 (1024^3: 18.95 -> 18.4 us), with 64-float slices
+//    from K >= 2048, where each k set's half of a 32-float slice is too
+//    little work between barriers (1024 x 1024 x 2048: 34.3 -> 33.2 us).
+//    Otherwise the four-wave form: with several work-groups per CU, or few
+//    K slices, the eight-wave form loses (1024 products of 64^3: 9.8 against
+//    16.2 us; 3072 x 3072 x 1024: 136.8 against 139.6 us).
 struct TileChoice {
   MfmaTile tile;
   bool long_k;
+  bool ksplit;
 };
 
 // Which matrix-core kernel:

@@ -15,13 +15,14 @@ namespace sgemm {
 // for every operand layout, so stored transposes give the plain layout's bits.
 //   C256     256 x 256 x 32, 2 x 4 waves of 128 x 64 (plain layout, 16-byte loads)
 //   C128     128 x 128 x 32, 4 x 2 waves of  32 x 64
-//   C64       64 x  64 x 32, 2 x 2 waves of  32 x 32, two k sets (8 waves)
-//   C64L      the same with 64-float K slices
+//   C64       64 x  64 x 32, 2 x 2 waves of  32 x 32 (4 waves)
+//   C64K2     the same with two k sets (8 waves)
+//   C64K2L    C64K2 with 64-float K slices
 //   C32x64    32 x  64 x 32, 1 x 2 waves of  32 x 32, two k sets (4 waves)
 //   C32x64L   the same with 64-float K slices
 //   C32       32 x  32 x 32, one wave, four k sets (4 waves)
 //   C32L      the same with 64-float K slices
-enum class DmaCfg { C256, C128, C64, C64L, C32x64, C32x64L, C32, C32L };
+enum class DmaCfg { C256, C128, C64, C64K2, C64K2L, C32x64, C32x64L, C32, C32L };
 
 struct DmaGeom {
   int bm, bn, bk;
@@ -32,7 +33,8 @@ inline DmaGeom dma_geom(DmaCfg c) {
     case DmaCfg::C256: return {256, 256, 32};
     case DmaCfg::C128: return {128, 128, 32};
     case DmaCfg::C64: return {64, 64, 32};
-    case DmaCfg::C64L: return {64, 64, 64};
+    case DmaCfg::C64K2: return {64, 64, 32};
+    case DmaCfg::C64K2L: return {64, 64, 64};
     case DmaCfg::C32x64: return {32, 64, 32};
     case DmaCfg::C32x64L: return {32, 64, 64};
     case DmaCfg::C32: return {32, 32, 32};
@@ -66,10 +68,14 @@ hipError_t launch_dma_layout(DmaCfg c, const GemmArgs &p, bool va, bool vb, hipS
                         PHASES>(p, va, vb, s, kGroupM);
       break;
     case DmaCfg::C64:
+      launch_dma_widths<64, 64, 32, 2, 2, SWZ, 1, TA, TB, 1, 2,
+                        PHASES>(p, va, vb, s, kGroupM);
+      break;
+    case DmaCfg::C64K2:
       launch_dma_widths<64, 64, 32, 2, 2, SWZ, 1, TA, TB, 2, 2,
                         PHASES>(p, va, vb, s, kGroupM);
       break;
-    case DmaCfg::C64L:
+    case DmaCfg::C64K2L:
       launch_dma_widths<64, 64, 64, 2, 2, SWZ, 1, TA, TB, 2, 2,
                         PHASES>(p, va, vb, s, kGroupM);
       break;

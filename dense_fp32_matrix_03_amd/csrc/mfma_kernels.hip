@@ -50,7 +50,8 @@ DmaCfg dma_cfg(TileChoice t, bool wide_plain) {
   switch (t.tile) {
     case MfmaTile::T256: return wide_plain ? DmaCfg::C256 : DmaCfg::C128;
     case MfmaTile::T128: return DmaCfg::C128;
-    case MfmaTile::T64: return t.long_k ? DmaCfg::C64L : DmaCfg::C64;
+    case MfmaTile::T64:
+      return !t.ksplit ? DmaCfg::C64 : (t.long_k ? DmaCfg::C64K2L : DmaCfg::C64K2);
     case MfmaTile::T32x64: return t.long_k ? DmaCfg::C32x64L : DmaCfg::C32x64;
     case MfmaTile::T32: return t.long_k ? DmaCfg::C32L : DmaCfg::C32;
   }
@@ -60,11 +61,17 @@ DmaCfg dma_cfg(TileChoice t, bool wide_plain) {
 }  // namespace
 
 TileChoice with_slice_rule(MfmaTile tile, long M, long N, long K, int cus, long batch) {
-  TileChoice c{tile, false};
-  if (tile == MfmaTile::T64) c.long_k = K >= 2048;
-  for (const TileShape &t : kTileShapes)
-    if (t.tile == tile && (tile == MfmaTile::T32x64 || tile == MfmaTile::T32))
-      c.long_k = tile_count(M, N, t.bm, t.bn, batch) <= cus;
+  TileChoice c{tile, false, false};
+  for (const TileShape &t : kTileShapes) {
+    if (t.tile != tile) continue;
+    const bool one_round = tile_count(M, N, t.bm, t.bn, batch) <= cus;
+    if (tile == MfmaTile::T64) {
+      c.ksplit = one_round && K >= 512;
+      c.long_k = c.ksplit && K >= 2048;
+    } else if (tile == MfmaTile::T32x64 || tile == MfmaTile::T32) {
+      c.long_k = one_round;
+    }
+  }
   return c;
 }
 

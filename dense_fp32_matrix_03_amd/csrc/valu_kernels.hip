@@ -3,9 +3,9 @@
 //   rung 0  one thread per output, operands straight from global memory
 //           (blog "【infra之路】03_动手写 CUDA Kernel", v1 Naive; article
 //           "硬件加速原理：CUDA核函数优化矩阵乘法的内存访问模式", basic kernel);
-//   rung 1  32 x 32 LDS tiles, one output per thread, zero-filled edges
-//           (blog v2 Shared Memory Tiled; textbook chapter "4. 矩阵乘法性能
-//           优化", section 三);
+//   rung 1  32 x 32 blocks through LDS with 64-wide K slices, one output
+//           per thread, 16-byte cooperative fetch, zero-filled edges
+//           (textbook chapter "4. 矩阵乘法性能优化", section 三);
 //   rung 2  128 x 128 x 16 block tiles, 256 threads, 8 x 8 outputs per thread
 //           as an outer product of 8 A and 8 B register values (chapter
 //           sections 一 and 二);
@@ -31,24 +31,55 @@ __global__ void __launch_bounds__(256) naive_kernel(GemmArgs p, int tiles_n) {
 }
 
 // ---------------------------------------------------------------- rung 1
-constexpr int kTile = 32;
+// Shared-memory tiling (textbook chapter "4. 矩阵乘法性能优化", section 三):
+// a work-group computes a 32 x 32 block of C, one output per thread, and
+// walks K in 64-wide slices; each slice of A and B is read from global
+// memory once per work-group into LDS and then reused by the 32 threads of
+// a row or column.  Every thread fetches one 16-byte chunk per slice --
+// threads 0-511 of A's 32 x 64 window, 512-1023 of B's 64 x 32 window
+// (SliceFetch, zero-filling outside the matrix) -- and A lands k-major, so
+// that in the k loop a wave's 64 lanes read one A value per row pair (a
+// broadcast) and 32 consecutive B values.
+constexpr int kTile = 32, kTileK = 64;
 
+template <bool VA, bool VB>
 __global__ void __launch_bounds__(kTile *kTile) lds_tiled_kernel(GemmArgs p, int tiles_n) {
-  __shared__ float sA[kTile][kTile];
-  __shared__ float sB[kTile][kTile];
-  const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;
-  const int bx = blockIdx.x % tiles_n, by = blockIdx.x / tiles_n;
-  const int row = by * kTile + ty, col = bx * kTile + tx;
+  constexpr int kHalf = kTile * kTile / 2;              // threads per operand
+  using FetchA = SliceFetch<kTile, kTileK, kHalf, VA>;  // 32 rows (m) x 64 k
+  using FetchB = SliceFetch<kTileK, kTile, kHalf, VB>;  // 64 rows (k) x 32 n
+  __shared__ float sAt[kTileK * (kTile + 1)];           // [k][m], rows padded by one
+  __shared__ __attribute__((aligned(16))) float sB[kTileK * kTile];  // [k][n]
+  const int tid = threadIdx.x;
+  const int m0 = (blockIdx.x / tiles_n) * kTile, n0 = (blockIdx.x % tiles_n) * kTile;
+  const int r = tid / kTile, c = tid % kTile;  // output row and column within the block
+  const bool fetch_a = tid < kHalf;
+  const int ft = fetch_a ? tid : tid - kHalf;  // index among the operand's fetch threads
+  FetchA fa;
+  FetchB fb;
+  if (fetch_a)
+    fa.init(p.A, p.lda, m0, 0, ft);
+  else
+    fb.init(p.B, p.ldb, 0, n0, ft);
   float sum = 0.f;
-  for (int k0 = 0; k0 < p.K; k0 += kTile) {
-    sA[ty][tx] = (row < p.M && k0 + tx < p.K) ? p.A[(long)row * p.lda + k0 + tx] : 0.f;
-    sB[ty][tx] = (k0 + ty < p.K && col < p.N) ? p.B[(long)(k0 + ty) * p.ldb + col] : 0.f;
+  for (int k0 = 0; k0 < p.K; k0 += kTileK) {
+    if (fetch_a) {
+      fa.load(p.M, p.K);
+      const int wr = FetchA::wrow(ft, 0), wc = FetchA::wcol(ft);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sAt[(wc + e) * (kTile + 1) + wr] = fa.v[0][e];
+      fa.advance(0, kTileK);
+    } else {
+      fb.load(p.K, p.N);
+      *reinterpret_cast<f32x4 *>(&sB[FetchB::wrow(ft, 0) * kTile + FetchB::wcol(ft)]) = fb.v[0];
+      fb.advance(kTileK, 0);
+    }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < kTile; ++k) sum = fmaf(sA[ty][k], sB[k][tx], sum);
+    for (int k = 0; k < kTileK; ++k)
+      sum = fmaf(sAt[k * (kTile + 1) + r], sB[k * kTile + c], sum);
     __syncthreads();
   }
-  if (row < p.M && col < p.N) p.C[(long)row * p.ldc + col] = sum;
+  if (m0 + r < p.M && n0 + c < p.N) p.C[(long)(m0 + r) * p.ldc + n0 + c] = sum;
 }
 
 // ---------------------------------------------------------------- rungs 2, 3
@@ -197,8 +228,15 @@ hipError_t launch_valu(int rung, const GemmArgs &p, bool va, bool vb, hipStream_
     }
     case 1: {
       const int tiles_n = (p.N + kTile - 1) / kTile, tiles_m = (p.M + kTile - 1) / kTile;
-      hipLaunchKernelGGL(lds_tiled_kernel, dim3((unsigned)((long)tiles_m * tiles_n)),
-                         dim3(kTile * kTile), 0, stream, p, tiles_n);
+      const dim3 grid((unsigned)((long)tiles_m * tiles_n)), block(kTile * kTile);
+      if (va && vb)
+        hipLaunchKernelGGL((lds_tiled_kernel<true, true>), grid, block, 0, stream, p, tiles_n);
+      else if (va)
+        hipLaunchKernelGGL((lds_tiled_kernel<true, false>), grid, block, 0, stream, p, tiles_n);
+      else if (vb)
+        hipLaunchKernelGGL((lds_tiled_kernel<false, true>), grid, block, 0, stream, p, tiles_n);
+      else
+        hipLaunchKernelGGL((lds_tiled_kernel<false, false>), grid, block, 0, stream, p, tiles_n);
       break;
     }
     case 2: launch_regtile<false>(p, va, vb, stream); break;

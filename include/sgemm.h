@@ -85,8 +85,9 @@ extern "C" {
  * that loses the least matrix-core time to partly filled rounds of
  * work-groups and to tile area outside C, the larger one when two come
  * within 3%.  The _MFMA_<n> variants force a tile instead (with the same
- * K-slice rule): the 64 x 64 tile runs two sets of four waves on the block,
- * the 32 x 64 tile two sets of two and the 32 x 32 tile four single waves,
+ * rule for its form): the 64 x 64 tile runs four waves, or two sets of four
+ * when its work-groups fit one round on the compute units and K >= 512; the
+ * 32 x 64 tile two sets of two waves and the 32 x 32 tile four single waves,
  * each set summing its share of every K slice; the sets' partial sums are
  * added in a fixed order.  SGEMM_VARIANT_MFMA_STAGED always fetches through
  * registers, SGEMM_VARIANT_MFMA_UNPADDED drops the LDS anti-conflict

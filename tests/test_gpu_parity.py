@@ -303,8 +303,8 @@ def test_load_paths_agree_bitwise(w, tile):
         assert outs[v].tobytes() == outs["mfma"].tobytes(), v
 
 
-@pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged", "reg", "dbuf",
-                                     "mfma_32", "mfma_dword", "mfma_32x64"])
+@pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged", "lds", "reg",
+                                     "dbuf", "mfma_32", "mfma_dword", "mfma_32x64"])
 def test_padded_leading_dimensions(variant):
     """NaN in the padding of A and B must not reach C; C's padding is untouched."""
     M, N, K = 200, 136, 72
@@ -319,7 +319,7 @@ def test_padded_leading_dimensions(variant):
     assert np.all(np.isnan(C[:, N:])), "C padding columns were written"
 
 
-@pytest.mark.parametrize("variant", ["mfma", "mfma_128", "dbuf"])
+@pytest.mark.parametrize("variant", ["mfma", "mfma_128", "lds", "dbuf"])
 def test_misaligned_pointers(variant):
     """Operands that start 4 bytes past a 16-byte boundary take the 32-bit path."""
     import torch
