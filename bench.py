@@ -362,7 +362,8 @@ def workload_table(variant) -> list[dict]:
     return rows
 
 
-LADDER = ("naive", "lds", "reg", "dbuf", "mfma_unpadded", "mfma_staged", "mfma_dword", "mfma")
+LADDER = ("naive", "lds", "reg", "dbuf", "mfma_unpadded", "mfma_staged", "mfma_dword",
+          "mfma_serial", "mfma")
 
 
 def ladder(w, steps: int, warmup: int, settle: float) -> list[dict]:

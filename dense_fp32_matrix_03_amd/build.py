@@ -35,7 +35,7 @@ LIB = os.path.join(PKG, "libsgemm.so")
 OBJDIR = os.path.join(PKG, "_build")
 SOURCES = ["api.hip", "mfma_kernels.hip", "mfma_layout_nn.hip", "mfma_layout_nn_unswizzled.hip",
            "mfma_layout_nt.hip", "mfma_layout_tn.hip", "mfma_layout_tt.hip",
-           "mfma_layout_nn_phases.hip", "mfma_staged.hip",
+           "mfma_layout_nn_phases.hip", "mfma_layout_nn_serial.hip", "mfma_staged.hip",
            "valu_kernels.hip", "vector_add.hip", "bf16x3.hip", "ceiling.hip", "noalloc.hip"]
 ARCH = "gfx950"
 BUNDLE_TARGET = f"hipv4-amdgcn-amd-amdhsa--{ARCH}"

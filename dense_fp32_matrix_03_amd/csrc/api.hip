@@ -191,6 +191,10 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
         // 4-byte loads for both operands whatever their alignment.
         err = sgemm::launch_mfma(autotile, MfmaPath::Auto, p, false, false, s);
         break;
+      case SGEMM_VARIANT_MFMA_SERIAL:
+        err = sgemm::launch_mfma(autotile, MfmaPath::Serial, p, va, vb, s);
+        if (err == hipErrorInvalidValue) return SGEMM_ERR_TOO_LARGE;  // no register-staged form
+        break;
       default:
         err = sgemm::launch_mfma(autotile, MfmaPath::Auto, p, va, vb, s);
         break;
@@ -482,6 +486,7 @@ const char *sgemm_variant_name(int variant) {
     case SGEMM_VARIANT_MFMA_UNPADDED: return "mfma_unpadded_lds";
     case SGEMM_VARIANT_MFMA_DWORD: return "mfma_dword_loads";
     case SGEMM_VARIANT_MFMA_32X64: return "mfma_32x64_ksplit2";
+    case SGEMM_VARIANT_MFMA_SERIAL: return "mfma_serial_race_triage";
     default: return nullptr;
   }
 }

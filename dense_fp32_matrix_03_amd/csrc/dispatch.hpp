@@ -38,7 +38,11 @@ struct TileChoice {
 //  Staged    register-staged loads always;
 //  Unpadded  as Auto but without the LDS anti-conflict layout (no A swizzle,
 //            no A row padding), to measure what that layout buys.
-enum class MfmaPath { Auto, Staged, Unpadded };
+// Auto: buffer-to-LDS (register-staged where a slice's offsets pass 32
+// bits); Staged: always register-staged; Unpadded: no LDS swizzle; Serial:
+// the race-triage schedule (hipErrorInvalidValue where Auto would fall back
+// to the register-staged kernel).
+enum class MfmaPath { Auto, Staged, Unpadded, Serial };
 
 // The tile for `batch` products of M x N on `cus` compute units: the one
 // that wastes the least matrix-core time to partly filled rounds of

@@ -45,54 +45,55 @@ inline DmaGeom dma_geom(DmaCfg c) {
 
 // Launch configuration c for operand layout (TA, TB); SWZ = false drops the
 // LDS swizzle; PHASES selects the diagnostic instantiation that writes
-// per-work-group timestamps to p.phases.  C256 is instantiated only for the
+// per-work-group timestamps to p.phases; SCHED = 2 the race-triage schedule
+// (no load in flight while a slice is computed; same bits).  C256 is instantiated only for the
 // plain layout with 16-byte loads on both operands (its other forms would
 // spill); asked for anything else it returns hipErrorInvalidValue.
-template <bool TA, bool TB, bool SWZ, bool PHASES = false>
+template <bool TA, bool TB, bool SWZ, bool PHASES = false, int SCHED = 1>
 hipError_t launch_dma_layout(DmaCfg c, const GemmArgs &p, bool va, bool vb, hipStream_t s);
 
-template <bool TA, bool TB, bool SWZ, bool PHASES>
+template <bool TA, bool TB, bool SWZ, bool PHASES, int SCHED>
 hipError_t launch_dma_layout(DmaCfg c, const GemmArgs &p, bool va, bool vb, hipStream_t s) {
   constexpr int kGroupM = 8;  // tile rows per raster group
   switch (c) {
     case DmaCfg::C256:
       if constexpr (!TA && !TB) {
         if (!(va && vb)) return hipErrorInvalidValue;
-        launch_dma_kernel<256, 256, 32, 2, 4, SWZ, 1, true, true, false, false, 1, 2, PHASES>(
+        launch_dma_kernel<256, 256, 32, 2, 4, SWZ, SCHED, true, true, false, false, 1, 2, PHASES>(
             p, s, kGroupM);
         return hipGetLastError();
       }
       return hipErrorInvalidValue;
     case DmaCfg::C128:
-      launch_dma_widths<128, 128, 32, 4, 2, SWZ, 1, TA, TB, 1, 2,
+      launch_dma_widths<128, 128, 32, 4, 2, SWZ, SCHED, TA, TB, 1, 2,
                         PHASES>(p, va, vb, s, kGroupM);
       break;
     case DmaCfg::C64:
-      launch_dma_widths<64, 64, 32, 2, 2, SWZ, 1, TA, TB, 1, 2,
+      launch_dma_widths<64, 64, 32, 2, 2, SWZ, SCHED, TA, TB, 1, 2,
                         PHASES>(p, va, vb, s, kGroupM);
       break;
     case DmaCfg::C64K2:
-      launch_dma_widths<64, 64, 32, 2, 2, SWZ, 1, TA, TB, 2, 2,
+      launch_dma_widths<64, 64, 32, 2, 2, SWZ, SCHED, TA, TB, 2, 2,
                         PHASES>(p, va, vb, s, kGroupM);
       break;
     case DmaCfg::C64K2L:
-      launch_dma_widths<64, 64, 64, 2, 2, SWZ, 1, TA, TB, 2, 2,
+      launch_dma_widths<64, 64, 64, 2, 2, SWZ, SCHED, TA, TB, 2, 2,
                         PHASES>(p, va, vb, s, kGroupM);
       break;
     case DmaCfg::C32x64:
-      launch_dma_widths<32, 64, 32, 1, 2, SWZ, 1, TA, TB, 2, 2,
+      launch_dma_widths<32, 64, 32, 1, 2, SWZ, SCHED, TA, TB, 2, 2,
                         PHASES>(p, va, vb, s, kGroupM);
       break;
     case DmaCfg::C32x64L:
-      launch_dma_widths<32, 64, 64, 1, 2, SWZ, 1, TA, TB, 2, 2,
+      launch_dma_widths<32, 64, 64, 1, 2, SWZ, SCHED, TA, TB, 2, 2,
                         PHASES>(p, va, vb, s, kGroupM);
       break;
     case DmaCfg::C32:
-      launch_dma_widths<32, 32, 32, 1, 1, SWZ, 1, TA, TB, 4, 2,
+      launch_dma_widths<32, 32, 32, 1, 1, SWZ, SCHED, TA, TB, 4, 2,
                         PHASES>(p, va, vb, s, kGroupM);
       break;
     case DmaCfg::C32L:
-      launch_dma_widths<32, 32, 64, 1, 1, SWZ, 1, TA, TB, 4, 2,
+      launch_dma_widths<32, 32, 64, 1, 1, SWZ, SCHED, TA, TB, 4, 2,
                         PHASES>(p, va, vb, s, kGroupM);
       break;
   }
@@ -113,5 +114,8 @@ extern template hipError_t launch_dma_layout<true, true, true, false>(DmaCfg, co
                                                                       bool, bool, hipStream_t);
 extern template hipError_t launch_dma_layout<false, false, true, true>(DmaCfg, const GemmArgs &,
                                                                        bool, bool, hipStream_t);
+extern template hipError_t launch_dma_layout<false, false, true, false, 2>(DmaCfg,
+                                                                          const GemmArgs &, bool,
+                                                                          bool, hipStream_t);
 
 }  // namespace sgemm

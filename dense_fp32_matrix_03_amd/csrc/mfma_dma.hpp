@@ -169,6 +169,15 @@ struct SliceGeom {
 // that ends slice t+1 waits only for slice t+1 -- NST-1 slices of latency
 // cover.  When K fits NST slices, every slice is in flight from the start.
 //
+// SCHED: 1 interleaves each group's loads and LDS reads with its
+// matrix-core instructions (the product kernel).  2 is the race-triage form:
+// no interleaving, and every slice is computed with no load in flight and
+// all waves in step -- a barrier that retires every buffer-to-LDS load after
+// each slice's loads are issued, after the prologue, and before each k group's
+// LDS reads.  Its matrix-core sequence is the product kernel's, so it gives
+// the same bits; a result that changes with SCHED points to a missing wait or
+// barrier (a race), one that does not to the arithmetic.
+//
 // PHASES (a diagnostic instantiation): thread 0 of each work-group writes
 // the reference-clock time (s_memrealtime) at five points of its run to
 // p.phases[8 w + i] -- 0 start, 1 first slice landed, 2 last slice
@@ -405,11 +414,13 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   // Slice t lives in stage S = t % NST; slices t+1 .. t+NST-1 are already on
   // their way to the other stages.
   constexpr int kLoadsPerSlice = GA::NBW + GB::NBW;  // per wave
+  static_assert(SCHED == 1 || SCHED == 2, "schedule 1 (interleaved) or 2 (race triage)");
   auto slice = [&](auto S, int t) {
     constexpr int s = decltype(S)::value;
     using SN = std::integral_constant<int, (s + 1) % NST>;
 #pragma unroll
     for (int g = 0; g < GW; ++g) {
+      if constexpr (SCHED == 2) dma_barrier();
       if (g + 1 < GW) {
         read_ops(S, g + 1, nxt);
         mma(cur);
@@ -419,6 +430,7 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         // loads of slices t+2 .. t+NST-1 may still be in flight).
         dma_barrier_keep<(NST - 2) * kLoadsPerSlice>();
         dma(S, t + NST);
+        if constexpr (SCHED == 2) dma_barrier();
         read_ops(SN(), 0, nxt);  // harmless if there is no slice t+1
         mma(cur);
         interleave(std::true_type());
@@ -429,7 +441,10 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
 
   static_for<NST>([&](auto S) { dma(S, decltype(S)::value); });
   // Slice 0 has landed; slices 1 .. NST-1 may still fly.
-  dma_barrier_keep<(NST - 1) * kLoadsPerSlice>();
+  if constexpr (SCHED == 2)
+    dma_barrier();
+  else
+    dma_barrier_keep<(NST - 1) * kLoadsPerSlice>();
   phase(1);
   read_ops(S0(), 0, cur);
   for (int t = 0; t < nk; t += NST) {

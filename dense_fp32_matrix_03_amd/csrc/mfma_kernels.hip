@@ -96,8 +96,12 @@ hipError_t launch_mfma(TileChoice tile, MfmaPath path, const GemmArgs &p, bool v
   const DmaGeom g = dma_geom(c);
   // A slice whose offsets pass a buffer descriptor's 32-bit range takes the
   // register-staged kernel (64-bit addressing).
-  if (!dma_offsets_fit(g.bm, p.lda, g.bk, p.ldb))
+  if (!dma_offsets_fit(g.bm, p.lda, g.bk, p.ldb)) {
+    if (path == MfmaPath::Serial) return hipErrorInvalidValue;
     return launch_staged(tile.tile, path != MfmaPath::Unpadded, p, va, vb, stream);
+  }
+  if (path == MfmaPath::Serial)
+    return launch_dma_layout<false, false, true, false, 2>(c, p, va, vb, stream);
   if (path == MfmaPath::Unpadded) return launch_dma_layout<false, false, false>(c, p, va, vb, stream);
   return launch_dma_layout<false, false, true>(c, p, va, vb, stream);
 }

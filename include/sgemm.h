@@ -96,6 +96,14 @@ extern "C" {
  * allowed (the article's coalescing section, "内存合并访问原理": the width
  * of each lane's access sets how many bytes one wave instruction moves):
  * all three exist to measure what those steps are worth.
+ * SGEMM_VARIANT_MFMA_SERIAL is a race-triage form of SGEMM_VARIANT_MFMA: the
+ * same tile, loads and matrix-core sequence, hence the same bits, but every
+ * K slice is computed with no load in flight and with extra workgroup
+ * barriers (after each slice's loads are issued and before each group of LDS
+ * reads; the chapter's section 四 explains the two barriers a pipelined
+ * slice needs).  A result that differs between the two points to a missing
+ * wait or barrier, one that does not to the arithmetic.  It returns
+ * SGEMM_ERR_TOO_LARGE where sgemm_run would fetch through registers.
  */
 #define SGEMM_VARIANT_NAIVE 0
 #define SGEMM_VARIANT_LDS 1
@@ -110,7 +118,8 @@ extern "C" {
 #define SGEMM_VARIANT_MFMA_32 10
 #define SGEMM_VARIANT_MFMA_DWORD 11
 #define SGEMM_VARIANT_MFMA_32X64 12
-#define SGEMM_NUM_VARIANTS 13
+#define SGEMM_VARIANT_MFMA_SERIAL 13
+#define SGEMM_NUM_VARIANTS 14
 
 /*
  * Initialise the library for the current device: checks that it is gfx950

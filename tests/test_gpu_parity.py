@@ -21,7 +21,7 @@ from dense_fp32_matrix_03_amd import inputs
 pytestmark = pytest.mark.gpu
 
 MFMA_VARIANTS = ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_staged", "mfma_unpadded",
-                 "mfma_32", "mfma_dword", "mfma_32x64"]
+                 "mfma_32", "mfma_dword", "mfma_32x64", "mfma_serial"]
 VALU_VARIANTS = ["naive", "lds", "reg", "dbuf"]
 ALL_VARIANTS = VALU_VARIANTS + MFMA_VARIANTS
 
@@ -238,7 +238,7 @@ EXTREME_SHAPES = [(1, 1, 1 << 22), (2, 3, 1 << 20), (1 << 20, 3, 7), (5, 1 << 20
 
 
 @pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged", "mfma_32",
-                                     "mfma_32x64"])
+                                     "mfma_32x64", "mfma_serial"])
 @pytest.mark.parametrize("shape", EXTREME_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_extreme_aspect_ratios(variant, shape):
     M, N, K = shape
@@ -259,7 +259,7 @@ DMA_DIMS = [4, 8, 12, 28, 36, 60, 68, 124, 132, 252, 260, 516]
 
 
 @pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_unpadded",
-                                     "mfma_32", "mfma_dword", "mfma_32x64"])
+                                     "mfma_32", "mfma_dword", "mfma_32x64", "mfma_serial"])
 def test_buffer_to_lds_edge_sweep(variant):
     g0 = np.random.default_rng(53 + MFMA_VARIANTS.index(variant))
     shapes = [tuple(int(x) for x in g0.choice(DMA_DIMS, 3)) for _ in range(20)]
@@ -451,6 +451,41 @@ def test_deterministic_bits_k_split_tile(M, N, K):
     assert not np.isnan(np.frombuffer(outs[0], dtype=np.float32)).any()
 
 
+# Shapes on which sgemm_run takes each buffer-to-LDS configuration on 256 CUs:
+# 32 x 32 with 64- and 32-float K slices, 32 x 64 with both, 64 x 64 in two k
+# sets with both, 64 x 64 in four waves, 128 x 128, 256 x 256; and a ragged
+# K, an unaligned A (lda = 777) and an odd-sized product.
+RACE_TRIAGE_SHAPES = [(256, 256, 256, 256), (768, 768, 768, 768), (640, 640, 2048, 2048),
+                      (1000, 1500, 776, 776), (1000, 1500, 777, 777), (1024, 1024, 1024, 1024),
+                      (1024, 1024, 2048, 2048), (3072, 3072, 1024, 1024),
+                      (2048, 2048, 2048, 2048), (4096, 4096, 1024, 1024), (300, 260, 100, 100),
+                      (129, 67, 45, 45)]
+
+
+@pytest.mark.parametrize("M,N,K,lda", RACE_TRIAGE_SHAPES, ids=lambda v: str(v))
+def test_race_triage_schedule_gives_the_same_bits(M, N, K, lda):
+    """SGEMM_VARIANT_MFMA_SERIAL computes every K slice with no load in flight
+    and all waves in step, on sgemm_run's tile and matrix-core sequence: the
+    two give identical bits (a difference would point to a race in the
+    pipelined schedule), and the result meets the tolerance."""
+    import torch
+    g = np.random.default_rng(M * 3 + N * 5 + K * 7)
+    A = inputs.padded(inputs.uniform(g, (M, K)), lda)
+    B = inputs.uniform(g, (K, N))
+    dA, dB = _dev(A), _dev(B)
+    outs = {}
+    for variant in ("mfma", "mfma_serial"):
+        dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        sg.sgemm_run_variant(variant, M, N, K, dA, lda, dB, N, dC, N)
+        torch.cuda.synchronize()
+        outs[variant] = dC.cpu().numpy()
+    assert outs["mfma_serial"].tobytes() == outs["mfma"].tobytes()
+    if M * N * K <= 1 << 30:
+        Cref, Sabs = oracle.sgemm_f64(A, B, K=K, N=N)
+        r = oracle.check(outs["mfma"], Cref, Sabs)
+        assert r.ok and r.usage < 0.05, str(r)
+
+
 # -- the phase-timestamp diagnostic ----------------------------------------------------
 
 @pytest.mark.parametrize("M,N,K,lda", [(256, 256, 256, 256), (1000, 1500, 777, 777),
@@ -626,6 +661,9 @@ def test_leading_dimension_past_32_bit_offsets():
     assert oracle.check(dC.cpu().numpy(), Cref, Sabs).ok
     with pytest.raises(sg.SgemmError) as e:
         sg.sgemm_run_ex(0, 0, M, N, K, 1.0, big, lda, dB, N, 0.0, dC, N)
+    assert e.value.status == sg._C["SGEMM_ERR_TOO_LARGE"]
+    with pytest.raises(sg.SgemmError) as e:  # the race-triage form has no register-staged kernel
+        sg.sgemm_run_variant("mfma_serial", M, N, K, big, lda, dB, N, dC, N)
     assert e.value.status == sg._C["SGEMM_ERR_TOO_LARGE"]
     nbytes = sg.sgemm_bf16x3_workspace_size(M, N, K)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
