@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     for n in ("sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_run_variant",
               "sgemm_run_ex", "sgemm_run_strided_batched", "vector_add", "sgemm_mfma_probe",
               "sgemm_bf16x3_workspace_size", "sgemm_run_bf16x3", "sgemm_run_bf16x3_ex",
-              "sgemm_mfma_ceiling", "sgemm_status_string", "sgemm_variant_name"):
+              "sgemm_mfma_ceiling", "sgemm_status_string", "sgemm_variant_name",
+              "sgemm_phase_times", "sgemm_run_bf16x3_ex_noalloc"):
         assert n in names
 
 
