@@ -158,8 +158,12 @@ def time_gpu(w, variant: str, steps: int, warmup: int, warm_seconds: float = 0.0
     stream = torch.cuda.current_stream()
     h = stream.cuda_stream
 
+    # Device addresses as ints: the binding's tensor checks would add host
+    # time per call that a product of a few microseconds cannot hide.
+    pa, pb, pc = dA.data_ptr(), dB.data_ptr(), dC.data_ptr()
+
     def step():
-        sg.sgemm_run_variant(variant, w.M, w.N, w.K, dA, w.lda, dB, w.ldb, dC, w.ldc, h)
+        sg.sgemm_run_variant(variant, w.M, w.N, w.K, pa, w.lda, pb, w.ldb, pc, w.ldc, h)
         _CALLS[0] += 1
 
     for _ in range(warmup):
@@ -460,12 +464,15 @@ def general_table(settle: float) -> list[dict]:
 # Tile sweep: (M, N, K, lda).  Small products, where the count of tiles
 # decides, and medium ones on either side of each switch of sgemm_run's tile
 # rule; 1000 x 1500 x 777 is the ragged workload (A rows not 16-byte aligned).
-SMALL = ((256, 256, 256, 256), (300, 260, 100, 100), (512, 512, 512, 512),
+SMALL = ((256, 256, 256, 256), (300, 260, 100, 100), (128, 128, 128, 128), (256, 256, 32, 32),
+         (768, 256, 256, 256), (256, 256, 1024, 1024), (512, 512, 64, 64), (512, 512, 128, 128),
+         (384, 384, 256, 256), (100, 3000, 64, 64), (640, 640, 128, 128), (512, 512, 256, 256),
+         (384, 384, 512, 512), (1000, 130, 1024, 1024), (512, 512, 512, 512),
          (768, 768, 768, 768), (640, 640, 2048, 2048), (1000, 130, 2048, 2048),
          (768, 1024, 512, 512), (832, 1024, 512, 512), (1024, 1024, 1024, 1024),
          (1000, 1500, 776, 776), (1000, 1500, 777, 777), (1536, 1536, 1536, 1536),
          (2048, 2048, 2048, 2048), (3072, 3072, 1024, 1024), (4096, 4096, 1024, 1024))
-SMALL_TILES = ("mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_32x64", "mfma_32")
+SMALL_TILES = ("mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_32x64", "mfma_32", "mfma_16")
 
 
 def small_table(steps: int, settle: float) -> list[dict]:
@@ -554,7 +561,7 @@ def phase_table(settle: float) -> list[dict]:
     back-to-back calls: first-slice latency, main loop, k-set reduction,
     stores; across work-groups the spread of their starts and the span from
     the first start to the last end; the shader clock; and the main loop's
-    matrix-core time at that clock (64 cycles per 32x32x2 instruction)."""
+    matrix-core time at that clock (32 multiply-adds per cycle per SIMD)."""
     import numpy as np
     import torch
 
@@ -593,8 +600,9 @@ def phase_table(settle: float) -> list[dict]:
 
         clock = float(np.mean((q[:, 6] - q[:, 5]) / np.maximum(q[:, 4] - q[:, 0], 1))) * REALTIME_MHZ
         kp = -(-K // bk) * bk
-        mfma_per_simd = (bm // 32) * (bn // 32) * (kp // 2) / 4
-        loop_mfma_us = mfma_per_simd * 64 / clock
+        # 32 multiply-adds per cycle per SIMD on either instruction (32x32x2
+        # in 64 cycles, 16x16x4 in 32); the tile's four SIMDs share the work.
+        loop_mfma_us = bm * bn * kp / 32 / 4 / clock
         r = {"M": M, "N": N, "K": K, "lda": lda, "tile": f"{bm}x{bn}x{bk}", "k_sets": ks,
              "workgroups": wgs, "call_us": round(ms * 1e3, 3),
              "span_us": round(float(q[:, 4].max() - q[:, 0].min()) * us, 3),

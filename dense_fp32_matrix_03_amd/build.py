@@ -35,7 +35,8 @@ LIB = os.path.join(PKG, "libsgemm.so")
 OBJDIR = os.path.join(PKG, "_build")
 SOURCES = ["api.hip", "mfma_kernels.hip", "mfma_layout_nn.hip", "mfma_layout_nn_unswizzled.hip",
            "mfma_layout_nt.hip", "mfma_layout_tn.hip", "mfma_layout_tt.hip",
-           "mfma_layout_nn_phases.hip", "mfma_layout_nn_serial.hip", "mfma_staged.hip",
+           "mfma_layout_nn_phases.hip", "mfma_layout_nn_serial.hip", "mfma_small.hip",
+           "mfma_staged.hip",
            "valu_kernels.hip", "vector_add.hip", "bf16x3.hip", "ceiling.hip", "noalloc.hip"]
 ARCH = "gfx950"
 BUNDLE_TARGET = f"hipv4-amdgcn-amd-amdhsa--{ARCH}"
@@ -127,8 +128,9 @@ def build(save_temps: str | None = None, resource_usage: bool = False,
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(lambda s: _compile(s, save_temps, resource_usage, verbose), srcs))
-    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-o", LIB + ".tmp", *objs], None,
-         verbose)
+    # -z defs: a symbol no object defines fails the link, not the first load.
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-Wl,-z,defs", "-o", LIB + ".tmp", *objs],
+         None, verbose)
     check_no_packed_f32(verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB

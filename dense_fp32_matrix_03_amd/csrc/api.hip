@@ -121,13 +121,15 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
   int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc);
   if (rc != SGEMM_OK) return rc;
   if (variant <= SGEMM_VARIANT_DBUF && !grid_fits(M, N, 1, 16, 16, 256)) return SGEMM_ERR_TOO_LARGE;
-  // Forced tiles: 512 threads per 64 x 64 block, 256 per 32 x 64 or 32 x 32
-  // block (sgemm_run only picks a tile whose launch fits).
+  // Forced tiles: 512 threads per 64 x 64 block, 256 per 32 x 64, 32 x 32 or
+  // 16 x 16 block (sgemm_run only picks a tile whose launch fits).
   if (variant == SGEMM_VARIANT_MFMA_64 && !grid_fits(M, N, 1, 64, 64, 512))
     return SGEMM_ERR_TOO_LARGE;
   if (variant == SGEMM_VARIANT_MFMA_32X64 && !grid_fits(M, N, 1, 32, 64, 256))
     return SGEMM_ERR_TOO_LARGE;
   if (variant == SGEMM_VARIANT_MFMA_32 && !grid_fits(M, N, 1, 32, 32, 256))
+    return SGEMM_ERR_TOO_LARGE;
+  if (variant == SGEMM_VARIANT_MFMA_16 && !grid_fits(M, N, 1, 16, 16, 256))
     return SGEMM_ERR_TOO_LARGE;
   if (!g_ready.load(std::memory_order_acquire)) return SGEMM_ERR_NOT_INITIALIZED;
   if (M == 0 || N == 0) return SGEMM_OK;
@@ -180,6 +182,9 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
         break;
       case SGEMM_VARIANT_MFMA_32:
         err = sgemm::launch_mfma(forced(MfmaTile::T32), MfmaPath::Auto, p, va, vb, s);
+        break;
+      case SGEMM_VARIANT_MFMA_16:
+        err = sgemm::launch_mfma(forced(MfmaTile::T16), MfmaPath::Auto, p, va, vb, s);
         break;
       case SGEMM_VARIANT_MFMA_STAGED:
         err = sgemm::launch_mfma(autotile, MfmaPath::Staged, p, va, vb, s);
@@ -487,6 +492,7 @@ const char *sgemm_variant_name(int variant) {
     case SGEMM_VARIANT_MFMA_DWORD: return "mfma_dword_loads";
     case SGEMM_VARIANT_MFMA_32X64: return "mfma_32x64_ksplit2";
     case SGEMM_VARIANT_MFMA_SERIAL: return "mfma_serial_race_triage";
+    case SGEMM_VARIANT_MFMA_16: return "mfma_16x16_ksplit4";
     default: return nullptr;
   }
 }

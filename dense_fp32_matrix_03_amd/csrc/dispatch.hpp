@@ -7,10 +7,12 @@
 
 namespace sgemm {
 
-// Block tiles of the matrix-core kernels (mfma_configs.hpp gives their wave
-// grids): 256 x 256, 128 x 128, 64 x 64, 32 x 64 (K split over two sets of
-// waves) and 32 x 32 (four k sets).
-enum class MfmaTile { T256, T128, T64, T32x64, T32 };
+// Block tiles of the matrix-core kernels (mfma_configs.hpp gives the wave
+// grids of the buffer-to-LDS kernel): 256 x 256, 128 x 128, 64 x 64, 32 x 64
+// (K split over two sets of waves) and 32 x 32 (four k sets); and 16 x 16,
+// the small-product kernel (mfma_small.hip: four k sets of one wave, operands
+// loaded straight into registers).
+enum class MfmaTile { T256, T128, T64, T32x64, T32, T16 };
 
 // A tile and its form.  long_k selects 64-float K slices; ksplit (64 x 64
 // only) runs the tile with two k sets of four waves.
@@ -25,6 +27,8 @@ enum class MfmaTile { T256, T128, T64, T32x64, T32 };
 //    Otherwise the four-wave form: with several work-groups per CU, or few
 //    K slices, the eight-wave form loses (1024 products of 64^3: 9.8 against
 //    16.2 us; 3072 x 3072 x 1024: 136.8 against 139.6 us).
+//  - The 16 x 16 tile has no K slices; where a variant runs the
+//    buffer-to-LDS kernel instead, it takes the 32 x 32 tile's form.
 struct TileChoice {
   MfmaTile tile;
   bool long_k;
@@ -32,23 +36,34 @@ struct TileChoice {
 };
 
 // Which matrix-core kernel:
-//  Auto      buffer-to-LDS loads (16 bytes per lane where va / vb, else
-//            4), or register-staged loads when a slice's offsets do not fit
-//            a buffer descriptor (a leading dimension near 2^29 or more);
-//  Staged    register-staged loads always;
-//  Unpadded  as Auto but without the LDS anti-conflict layout (no A swizzle,
-//            no A row padding), to measure what that layout buys.
-// Auto: buffer-to-LDS (register-staged where a slice's offsets pass 32
-// bits); Staged: always register-staged; Unpadded: no LDS swizzle; Serial:
-// the race-triage schedule (hipErrorInvalidValue where Auto would fall back
-// to the register-staged kernel).
+//  Auto      the 16 x 16 tile's small-product kernel; else buffer-to-LDS
+//            loads (16 bytes per lane where va / vb, else 4), or
+//            register-staged loads when a slice's offsets do not fit a
+//            buffer descriptor (a leading dimension near 2^29 or more);
+//  Staged    register-staged loads always (the 16 x 16 tile takes 64 x 64);
+//  Unpadded  buffer-to-LDS without the LDS anti-conflict layout (no A
+//            swizzle), to measure what that layout buys (the 16 x 16 tile
+//            takes 32 x 32);
+//  Serial    the race-triage schedule of the buffer-to-LDS kernel
+//            (hipErrorInvalidValue where Auto would fall back to the
+//            register-staged kernel); the small-product kernel stages
+//            nothing through LDS and runs unchanged.
 enum class MfmaPath { Auto, Staged, Unpadded, Serial };
 
-// The tile for `batch` products of M x N on `cus` compute units: the one
-// that wastes the least matrix-core time to partly filled rounds of
-// work-groups and to tile area outside C, preferring the larger tile when
-// two come within 3% of each other.
+// The tile for `batch` products of M x N x K on `cus` compute units: the
+// buffer-to-LDS tile that wastes the least matrix-core time to partly filled
+// rounds of work-groups and to tile area outside C, preferring the larger
+// tile when two come within 3% of each other -- unless small_product()
+// holds and either the 16 x 16 tiles read at most 64 KiB per compute unit
+// or that best tile keeps under 90% of the matrix-core time on C: then the
+// 16 x 16 tile.
 TileChoice choose_mfma_tile(long M, long N, long K, int cus, long batch = 1);
+
+// Whether the 16 x 16 small-product kernel serves the product: K <= 1024,
+// at most 8 of its tiles per compute unit, and its tiles' operand reads
+// (128 K bytes per tile, each wave loading its own) at most 128 KiB per
+// compute unit.
+bool small_product(long M, long N, long K, int cus, long batch = 1);
 
 // `tile` with the K-slice length choose_mfma_tile would give it.
 TileChoice with_slice_rule(MfmaTile tile, long M, long N, long K, int cus, long batch = 1);
@@ -63,12 +78,23 @@ hipError_t launch_mfma(TileChoice tile, MfmaPath path, const GemmArgs &p, bool v
 hipError_t launch_mfma_general(TileChoice tile, const GemmArgs &p, bool ta, bool tb, bool va,
                                bool vb, hipStream_t stream);
 
-// sgemm_run's buffer-to-LDS computation of the plain product with phase
-// timestamps in p.phases (8 per work-group); *workgroups receives the
-// launch's work-group count.  With p.phases null nothing is launched.
-// hipErrorInvalidValue if a slice's offsets do not fit a buffer descriptor.
+// sgemm_run's computation of the plain product with phase timestamps in
+// p.phases (8 per work-group); *workgroups receives the launch's work-group
+// count.  With p.phases null nothing is launched.  hipErrorInvalidValue if a
+// slice's offsets do not fit a buffer descriptor.
 hipError_t launch_mfma_phases(TileChoice tile, const GemmArgs &p, bool va, bool vb,
                               long *workgroups, hipStream_t stream);
+
+// Small-product kernel (mfma_small.hip) over p.batch products: 16 x 16 tiles,
+// four k sets of one wave, operands loaded straight into registers (ta / tb:
+// A / B stored transposed; va / vb: the operand qualifies for 16-byte loads).
+// Any K (in chunks of 1024 beyond that).
+hipError_t launch_small(const GemmArgs &p, bool ta, bool tb, bool va, bool vb,
+                        hipStream_t stream);
+// The same for the plain layout with phase timestamps in p.phases.
+hipError_t launch_small_phases(const GemmArgs &p, bool va, hipStream_t stream);
+// Work-groups of the small-product kernel for `batch` products of M x N.
+long small_workgroups(long M, long N, long batch);
 
 // Register-staged kernel (mfma_gemm.hpp) on a 256, 128 or 64 tile (others
 // take 64); padded = false drops its A row padding.

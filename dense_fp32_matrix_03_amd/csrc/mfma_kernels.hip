@@ -1,7 +1,7 @@
 // mfma_kernels.hip -- the choice of matrix-core configuration for a call,
-// the dispatch to the per-layout launchers (mfma_configs.hpp,
-// mfma_layout_*.hip) and the register-staged fallback, and the
-// one-instruction layout probe.
+// the dispatch to the small-product kernel (mfma_small.hip), the per-layout
+// launchers of the buffer-to-LDS kernel (mfma_configs.hpp, mfma_layout_*.hip)
+// and the register-staged fallback, and the one-instruction layout probe.
 #include <math.h>
 
 #include "common.hpp"
@@ -23,7 +23,8 @@ constexpr TileShape kTileShapes[] = {{MfmaTile::T256, 256, 256, 512},
                                      {MfmaTile::T128, 128, 128, 512},
                                      {MfmaTile::T64, 64, 64, 512},
                                      {MfmaTile::T32x64, 32, 64, 256},
-                                     {MfmaTile::T32, 32, 32, 256}};
+                                     {MfmaTile::T32, 32, 32, 256},
+                                     {MfmaTile::T16, 16, 16, 256}};
 
 // A launch's work-items (work-groups x threads) must fit 32 bits.
 constexpr double kMaxWorkItems = 4294967295.0;
@@ -53,22 +54,41 @@ DmaCfg dma_cfg(TileChoice t, bool wide_plain) {
     case MfmaTile::T64:
       return !t.ksplit ? DmaCfg::C64 : (t.long_k ? DmaCfg::C64K2L : DmaCfg::C64K2);
     case MfmaTile::T32x64: return t.long_k ? DmaCfg::C32x64L : DmaCfg::C32x64;
+    case MfmaTile::T16:  // a variant that runs the buffer-to-LDS kernel instead
     case MfmaTile::T32: return t.long_k ? DmaCfg::C32L : DmaCfg::C32;
   }
   return DmaCfg::C128;
 }
 
+// Operand bytes per compute unit that the 16 x 16 tiles read: a 16-row
+// strip of op(A) and a 16-column strip of op(B) per tile, each wave loading
+// its own share.
+double small_bytes_per_cu(long M, long N, long K, int cus, long batch) {
+  return (double)tile_count(M, N, 16, 16, batch) * (double)K * (2.0 * 16 * 4) / cus;
+}
+
 }  // namespace
+
+bool small_product(long M, long N, long K, int cus, long batch) {
+  constexpr long kMaxK = 1024;
+  constexpr double kMaxTilesPerCu = 8.0;
+  constexpr double kMaxBytesPerCu = 128.0 * 1024;
+  return K <= kMaxK && (double)tile_count(M, N, 16, 16, batch) <= kMaxTilesPerCu * cus &&
+         small_bytes_per_cu(M, N, K, cus, batch) <= kMaxBytesPerCu;
+}
 
 TileChoice with_slice_rule(MfmaTile tile, long M, long N, long K, int cus, long batch) {
   TileChoice c{tile, false, false};
+  // The 16 x 16 tile, where a variant runs it on the buffer-to-LDS kernel,
+  // takes the 32 x 32 tile's form.
+  const MfmaTile form = tile == MfmaTile::T16 ? MfmaTile::T32 : tile;
   for (const TileShape &t : kTileShapes) {
-    if (t.tile != tile) continue;
+    if (t.tile != form) continue;
     const bool one_round = tile_count(M, N, t.bm, t.bn, batch) <= cus;
-    if (tile == MfmaTile::T64) {
+    if (form == MfmaTile::T64) {
       c.ksplit = one_round && K >= 512;
       c.long_k = c.ksplit && K >= 2048;
-    } else if (tile == MfmaTile::T32x64 || tile == MfmaTile::T32) {
+    } else if (form == MfmaTile::T32x64 || form == MfmaTile::T32) {
       c.long_k = one_round;
     }
   }
@@ -79,19 +99,36 @@ TileChoice with_slice_rule(MfmaTile tile, long M, long N, long K, int cus, long 
 // takes 32 x 64 (768 tiles, three full rounds: 31.9 -> 25.4 us against
 // 64 x 64, whose 384 tiles leave half the CUs idle in the second round);
 // 1024^3 takes 64 x 64 (256 tiles); 2048^3 128 x 128; 8192^3 256 x 256;
-// 256^3, 512^3 and 1000 x 130 x 2048 take 32 x 32.
+// 512^3 and 1000 x 130 x 2048 take 32 x 32; 256^3 16 x 16.
+//
+// The 16 x 16 small-product tile, measured on 256 CUs against the best
+// buffer-to-LDS tile (kernel trace): 256^3 5.49 -> 3.77 us, 256 x 256 x 1024
+// 8.22 -> 6.77, 512 x 512 x 64 4.80 -> 3.91, 512 x 512 x 128 5.36 -> 4.79,
+// 384 x 384 x 256 5.47 -> 5.14, 100 x 3000 x 64 5.31 -> 4.36.  It loses once
+// its tiles read more than 128 KiB per CU (384 x 384 x 512: 7.55 against
+// 6.61; 1000 x 130 x 1024: 16.62 against 10.16), and at 64-128 KiB per CU
+// against a buffer-to-LDS tile that fills the CUs (512 x 512 x 256: 6.08
+// against 5.65).  Shapes with more than 8 of its tiles per CU were not
+// measured.
 TileChoice choose_mfma_tile(long M, long N, long K, int cus, long batch) {
+  auto eff = [&](const TileShape &t) {
+    return t.tile == MfmaTile::T16 ? 0.0 : tile_efficiency(t, M, N, cus, batch);
+  };
   double best = 0.0;
-  for (const TileShape &t : kTileShapes) best = fmax(best, tile_efficiency(t, M, N, cus, batch));
+  for (const TileShape &t : kTileShapes) best = fmax(best, eff(t));
+  if (small_product(M, N, K, cus, batch) &&
+      (small_bytes_per_cu(M, N, K, cus, batch) <= 64.0 * 1024 || best < 0.9))
+    return with_slice_rule(MfmaTile::T16, M, N, K, cus, batch);
   for (const TileShape &t : kTileShapes)
-    if (best > 0.0 && tile_efficiency(t, M, N, cus, batch) >= 0.97 * best)
-      return with_slice_rule(t.tile, M, N, K, cus, batch);
+    if (best > 0.0 && eff(t) >= 0.97 * best) return with_slice_rule(t.tile, M, N, K, cus, batch);
   return with_slice_rule(MfmaTile::T128, M, N, K, cus, batch);
 }
 
 hipError_t launch_mfma(TileChoice tile, MfmaPath path, const GemmArgs &p, bool va, bool vb,
                        hipStream_t stream) {
   if (path == MfmaPath::Staged) return launch_staged(tile.tile, true, p, va, vb, stream);
+  if (tile.tile == MfmaTile::T16 && path != MfmaPath::Unpadded)
+    return launch_small(p, false, false, va, vb, stream);
   const DmaCfg c = dma_cfg(tile, va && vb);
   const DmaGeom g = dma_geom(c);
   // A slice whose offsets pass a buffer descriptor's 32-bit range takes the
@@ -108,6 +145,10 @@ hipError_t launch_mfma(TileChoice tile, MfmaPath path, const GemmArgs &p, bool v
 
 hipError_t launch_mfma_phases(TileChoice tile, const GemmArgs &p, bool va, bool vb,
                               long *workgroups, hipStream_t stream) {
+  if (tile.tile == MfmaTile::T16) {
+    *workgroups = small_workgroups(p.M, p.N, 1);
+    return p.phases == nullptr ? hipSuccess : launch_small_phases(p, va, stream);
+  }
   const DmaCfg c = dma_cfg(tile, va && vb);
   const DmaGeom g = dma_geom(c);
   if (!dma_offsets_fit(g.bm, p.lda, g.bk, p.ldb)) return hipErrorInvalidValue;
@@ -118,6 +159,7 @@ hipError_t launch_mfma_phases(TileChoice tile, const GemmArgs &p, bool va, bool 
 
 hipError_t launch_mfma_general(TileChoice tile, const GemmArgs &p, bool ta, bool tb, bool va,
                                bool vb, hipStream_t stream) {
+  if (tile.tile == MfmaTile::T16) return launch_small(p, ta, tb, va, vb, stream);
   const DmaCfg c = dma_cfg(tile, !ta && !tb && va && vb);
   const DmaGeom g = dma_geom(c);
   if (!dma_offsets_fit(ta ? g.bk : g.bm, p.lda, tb ? g.bn : g.bk, p.ldb))

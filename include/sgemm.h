@@ -46,8 +46,9 @@
  * with at most 2^24 blocks of 64 x 64 (counting every product of a batch)
  * and pick a tile whose launch fits; the forced tiles need 512 work-items
  * per 64 x 64 block (SGEMM_VARIANT_MFMA_64) or 256 per 32 x 64
- * (SGEMM_VARIANT_MFMA_32X64) or 32 x 32 block (SGEMM_VARIANT_MFMA_32), the
- * vector-FMA variants 256 per 16 x 16 block.
+ * (SGEMM_VARIANT_MFMA_32X64), 32 x 32 (SGEMM_VARIANT_MFMA_32) or 16 x 16
+ * block (SGEMM_VARIANT_MFMA_16), the vector-FMA variants 256 per 16 x 16
+ * block.
  *
  * Threads.  sgemm_create / sgemm_destroy are serialised internally;
  * sgemm_run may be called from any thread once sgemm_create has succeeded.
@@ -81,15 +82,21 @@ extern "C" {
  * the operand is 16-byte aligned with a leading dimension and width that are
  * multiples of 4, else 4 bytes; only an operand whose leading dimension puts
  * one slice beyond 2 GiB is fetched through registers instead.  sgemm_run
- * picks the block tile (256 x 256, 128 x 128, 64 x 64, 32 x 64 or 32 x 32)
- * that loses the least matrix-core time to partly filled rounds of
+ * picks the block tile (256 x 256, 128 x 128, 64 x 64, 32 x 64, 32 x 32 or
+ * 16 x 16) that loses the least matrix-core time to partly filled rounds of
  * work-groups and to tile area outside C, the larger one when two come
- * within 3%.  The _MFMA_<n> variants force a tile instead (with the same
- * rule for its form): the 64 x 64 tile runs four waves, or two sets of four
- * when its work-groups fit one round on the compute units and K >= 512; the
+ * within 3%.  A product with K <= 1024, at most 8 tiles of 16 x 16 per
+ * compute unit and at most 128 KiB of operand reads per compute unit on
+ * those tiles (128 K bytes per tile) takes the 16 x 16 tile instead when
+ * those reads stay within 64 KiB per compute unit or the best of the other
+ * tiles would spend under 90% of the matrix-core time on C.  The _MFMA_<n> variants force a tile instead (with the same rule
+ * for its form): the 64 x 64 tile runs four waves, or two sets of four when
+ * its work-groups fit one round on the compute units and K >= 512; the
  * 32 x 64 tile two sets of two waves and the 32 x 32 tile four single waves,
- * each set summing its share of every K slice; the sets' partial sums are
- * added in a fixed order.  SGEMM_VARIANT_MFMA_STAGED always fetches through
+ * each set summing its share of every K slice; the 16 x 16 tile (the
+ * 16x16x4 matrix instruction) four single waves that load their share of K
+ * straight from global memory into registers, with no LDS staging; the
+ * sets' partial sums are added in a fixed order.  SGEMM_VARIANT_MFMA_STAGED always fetches through
  * registers, SGEMM_VARIANT_MFMA_UNPADDED drops the LDS anti-conflict
  * layout (the chapter's padding, section 三), and SGEMM_VARIANT_MFMA_DWORD
  * fetches both operands 4 bytes per lane even where 16-byte loads are
@@ -103,7 +110,9 @@ extern "C" {
  * reads; the chapter's section 四 explains the two barriers a pipelined
  * slice needs).  A result that differs between the two points to a missing
  * wait or barrier, one that does not to the arithmetic.  It returns
- * SGEMM_ERR_TOO_LARGE where sgemm_run would fetch through registers.
+ * SGEMM_ERR_TOO_LARGE where sgemm_run would fetch through registers.  The
+ * 16 x 16 tile stages nothing through LDS and runs unchanged; the
+ * register-staged and unswizzled variants run it as 64 x 64 and 32 x 32.
  */
 #define SGEMM_VARIANT_NAIVE 0
 #define SGEMM_VARIANT_LDS 1
@@ -119,7 +128,8 @@ extern "C" {
 #define SGEMM_VARIANT_MFMA_DWORD 11
 #define SGEMM_VARIANT_MFMA_32X64 12
 #define SGEMM_VARIANT_MFMA_SERIAL 13
-#define SGEMM_NUM_VARIANTS 14
+#define SGEMM_VARIANT_MFMA_16 14
+#define SGEMM_NUM_VARIANTS 15
 
 /*
  * Initialise the library for the current device: checks that it is gfx950

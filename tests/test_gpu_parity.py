@@ -21,7 +21,7 @@ from dense_fp32_matrix_03_amd import inputs
 pytestmark = pytest.mark.gpu
 
 MFMA_VARIANTS = ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_staged", "mfma_unpadded",
-                 "mfma_32", "mfma_dword", "mfma_32x64", "mfma_serial"]
+                 "mfma_32", "mfma_dword", "mfma_32x64", "mfma_serial", "mfma_16"]
 VALU_VARIANTS = ["naive", "lds", "reg", "dbuf"]
 ALL_VARIANTS = VALU_VARIANTS + MFMA_VARIANTS
 
@@ -238,7 +238,7 @@ EXTREME_SHAPES = [(1, 1, 1 << 22), (2, 3, 1 << 20), (1 << 20, 3, 7), (5, 1 << 20
 
 
 @pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged", "mfma_32",
-                                     "mfma_32x64", "mfma_serial"])
+                                     "mfma_32x64", "mfma_serial", "mfma_16"])
 @pytest.mark.parametrize("shape", EXTREME_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_extreme_aspect_ratios(variant, shape):
     M, N, K = shape
@@ -259,7 +259,8 @@ DMA_DIMS = [4, 8, 12, 28, 36, 60, 68, 124, 132, 252, 260, 516]
 
 
 @pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_unpadded",
-                                     "mfma_32", "mfma_dword", "mfma_32x64", "mfma_serial"])
+                                     "mfma_32", "mfma_dword", "mfma_32x64", "mfma_serial",
+                                     "mfma_16"])
 def test_buffer_to_lds_edge_sweep(variant):
     g0 = np.random.default_rng(53 + MFMA_VARIANTS.index(variant))
     shapes = [tuple(int(x) for x in g0.choice(DMA_DIMS, 3)) for _ in range(20)]
@@ -304,7 +305,7 @@ def test_load_paths_agree_bitwise(w, tile):
 
 
 @pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged", "lds", "reg",
-                                     "dbuf", "mfma_32", "mfma_dword", "mfma_32x64"])
+                                     "dbuf", "mfma_32", "mfma_dword", "mfma_32x64", "mfma_16"])
 def test_padded_leading_dimensions(variant):
     """NaN in the padding of A and B must not reach C; C's padding is untouched."""
     M, N, K = 200, 136, 72
@@ -319,7 +320,7 @@ def test_padded_leading_dimensions(variant):
     assert np.all(np.isnan(C[:, N:])), "C padding columns were written"
 
 
-@pytest.mark.parametrize("variant", ["mfma", "mfma_128", "lds", "dbuf"])
+@pytest.mark.parametrize("variant", ["mfma", "mfma_128", "lds", "dbuf", "mfma_16"])
 def test_misaligned_pointers(variant):
     """Operands that start 4 bytes past a 16-byte boundary take the 32-bit path."""
     import torch
@@ -348,39 +349,63 @@ def test_misaligned_pointers(variant):
 # CUs)), the larger one when two come within 3%; a tile whose launch would
 # pass 2^32 work-items is out.
 TILE_RULE = [("mfma_256", 256, 256, 512), ("mfma_128", 128, 128, 512), ("mfma_64", 64, 64, 512),
-             ("mfma_32x64", 32, 64, 256), ("mfma_32", 32, 32, 256)]
+             ("mfma_32x64", 32, 64, 256), ("mfma_32", 32, 32, 256), ("mfma_16", 16, 16, 256)]
 
 
-def _expected_tile(M, N, batch, cus):
-    def eff(bm, bn, threads):
+def _small_product(M, N, K, batch, cus):
+    """The 16 x 16 tile serves K <= 1024 with at most 8 of its tiles per CU
+    and at most 128 KiB of operand reads per CU (128 K bytes per tile)."""
+    tiles = -(-M // 16) * -(-N // 16) * batch
+    return K <= 1024 and tiles <= 8 * cus and tiles * K * 128 <= 128 * 1024 * cus
+
+
+def _expected_tile(M, N, K, batch, cus):
+    def eff(name, bm, bn, threads):
+        if name == "mfma_16":
+            return 0.0
         tiles = -(-M // bm) * -(-N // bn) * batch
         if tiles * threads > 2 ** 32 - 1:
             return 0.0
         rounds = -(-tiles // cus)
         return float(M) * N * batch / (rounds * cus * bm * bn)
-    best = max(eff(bm, bn, t) for _, bm, bn, t in TILE_RULE)
-    for name, bm, bn, t in TILE_RULE:
-        if eff(bm, bn, t) >= 0.97 * best:
-            return name
+    best = max(eff(*t) for t in TILE_RULE)
+    tiles16 = -(-M // 16) * -(-N // 16) * batch
+    if _small_product(M, N, K, batch, cus) and (tiles16 * K * 128 <= 64 * 1024 * cus
+                                                 or best < 0.9):
+        return "mfma_16"
+    for t in TILE_RULE:
+        if eff(*t) >= 0.97 * best:
+            return t[0]
     return "mfma_128"
 
 
 def test_expected_tile_on_256_cus():
     """The restated rule on 256 CUs picks the tiles measured best."""
-    assert _expected_tile(256, 256, 1, 256) == "mfma_32"
-    assert _expected_tile(512, 512, 1, 256) == "mfma_32"
-    assert _expected_tile(1000, 130, 1, 256) == "mfma_32"
-    assert _expected_tile(1000, 1500, 1, 256) == "mfma_32x64"
-    assert _expected_tile(1024, 1024, 1, 256) == "mfma_64"
-    assert _expected_tile(2048, 2048, 1, 256) == "mfma_128"
-    assert _expected_tile(8192, 8192, 1, 256) == "mfma_256"
-    assert _expected_tile(64, 64, 1024, 256) == "mfma_64"
+    assert _expected_tile(256, 256, 256, 1, 256) == "mfma_16"
+    assert _expected_tile(300, 260, 100, 1, 256) == "mfma_16"
+    assert _expected_tile(768, 256, 256, 1, 256) == "mfma_16"
+    assert _expected_tile(512, 512, 64, 1, 256) == "mfma_16"
+    assert _expected_tile(512, 512, 128, 1, 256) == "mfma_16"    # 64 KiB per CU
+    assert _expected_tile(512, 512, 256, 1, 256) == "mfma_32"    # 128 KiB, 32 x 32 fills the CUs
+    assert _expected_tile(256, 256, 1024, 1, 256) == "mfma_16"   # at the traffic bound
+    assert _expected_tile(384, 384, 512, 1, 256) == "mfma_32"    # over it
+    assert _expected_tile(2048, 2048, 8, 1, 256) == "mfma_128"   # over 8 tiles per CU
+    assert _expected_tile(512, 512, 512, 1, 256) == "mfma_32"
+    assert _expected_tile(1000, 130, 1024, 1, 256) == "mfma_32"
+    assert _expected_tile(1000, 130, 2048, 1, 256) == "mfma_32"
+    assert _expected_tile(1000, 1500, 777, 1, 256) == "mfma_32x64"
+    assert _expected_tile(1024, 1024, 1024, 1, 256) == "mfma_64"
+    assert _expected_tile(2048, 2048, 2048, 1, 256) == "mfma_128"
+    assert _expected_tile(8192, 8192, 8192, 1, 256) == "mfma_256"
+    assert _expected_tile(64, 64, 64, 1024, 256) == "mfma_64"
 
 
 @pytest.mark.parametrize("M,N,K,batch", [
     (512, 512, 512, 1), (256, 256, 256, 1), (300, 260, 100, 1), (1000, 130, 2048, 1),
     (1024, 1024, 256, 1), (64, 64, 64, 256), (128, 128, 128, 8), (768, 1024, 512, 1),
-    (832, 1024, 512, 1), (1000, 1500, 776, 1), (640, 640, 2048, 1), (3072, 3072, 64, 1)])
+    (832, 1024, 512, 1), (1000, 1500, 776, 1), (640, 640, 2048, 1), (3072, 3072, 64, 1),
+    (768, 256, 256, 1), (256, 256, 1024, 1), (384, 384, 512, 1), (64, 64, 1024, 1),
+    (512, 512, 64, 1)])
 def test_tile_choice(M, N, K, batch):
     """sgemm_run takes the tile of the rule above on this device's CU count:
     its bits equal those of that forced tile (same K-slice rule), and both
@@ -388,7 +413,7 @@ def test_tile_choice(M, N, K, batch):
     last products."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    tile = _expected_tile(M, N, batch, cus)
+    tile = _expected_tile(M, N, K, batch, cus)
     g = np.random.default_rng(M + N + K + batch)
     A = inputs.uniform(g, (batch, M, K))
     B = inputs.uniform(g, (batch, K, N))
@@ -451,11 +476,14 @@ def test_deterministic_bits_k_split_tile(M, N, K):
     assert not np.isnan(np.frombuffer(outs[0], dtype=np.float32)).any()
 
 
-# Shapes on which sgemm_run takes each buffer-to-LDS configuration on 256 CUs:
-# 32 x 32 with 64- and 32-float K slices, 32 x 64 with both, 64 x 64 in two k
-# sets with both, 64 x 64 in four waves, 128 x 128, 256 x 256; and a ragged
-# K, an unaligned A (lda = 777) and an odd-sized product.
-RACE_TRIAGE_SHAPES = [(256, 256, 256, 256), (768, 768, 768, 768), (640, 640, 2048, 2048),
+# Shapes on which sgemm_run takes each configuration on 256 CUs: the 16 x 16
+# small-product tile (no LDS pipeline: the race-triage form runs it
+# unchanged); 32 x 32 with 64- and 32-float K slices, 32 x 64 with both,
+# 64 x 64 in two k sets with both, 64 x 64 in four waves, 128 x 128,
+# 256 x 256; and a ragged K, an unaligned A (lda = 777) and an odd-sized
+# product.
+RACE_TRIAGE_SHAPES = [(256, 256, 256, 256), (512, 512, 512, 512), (768, 768, 768, 768),
+                      (640, 640, 2048, 2048),
                       (1000, 1500, 776, 776), (1000, 1500, 777, 777), (1024, 1024, 1024, 1024),
                       (1024, 1024, 2048, 2048), (3072, 3072, 1024, 1024),
                       (2048, 2048, 2048, 2048), (4096, 4096, 1024, 1024), (300, 260, 100, 100),
@@ -517,7 +545,7 @@ def test_phase_times_diagnostic(M, N, K, lda):
     tile = int(q[0, 7])
     assert np.all(q[:, 7] == tile)
     bm, bn, bk, ks = tile & 0xffff, (tile >> 16) & 0xffff, (tile >> 32) & 0xffff, tile >> 48
-    assert -(-M // bm) * -(-N // bn) == wgs and bk in (32, 64) and ks in (1, 2, 4)
+    assert -(-M // bm) * -(-N // bn) == wgs and bk % 16 == 0 and ks in (1, 2, 4)
 
 
 # -- degenerate sizes and errors --------------------------------------------------------
@@ -640,13 +668,15 @@ def test_host_threads():
 
 
 def test_leading_dimension_past_32_bit_offsets():
-    """lda = 2^30 + 8: a 64-row slice of A spans more than a buffer
-    descriptor's 2 GiB, so sgemm_run falls back to the register-staged kernel
-    (64-bit addressing); the general entry point reports SGEMM_ERR_TOO_LARGE
+    """lda = 2^30 + 8: a 32-row slice of A spans more than a buffer
+    descriptor's 2 GiB, so sgemm_run (on the 32 x 32 tile: K = 1100 is past
+    the 16 x 16 tile's K) falls back to the register-staged kernel (64-bit
+    addressing); the general entry point reports SGEMM_ERR_TOO_LARGE, the
+    16 x 16 small-product kernel (64-bit addressing, no buffer descriptors)
     and the bfloat16-split path (which reads A in its own split kernel)
-    computes it."""
+    compute it."""
     import torch
-    M, N, K, lda = 3, 48, 64, (1 << 30) + 8
+    M, N, K, lda = 3, 48, 1100, (1 << 30) + 8
     g = np.random.default_rng(53)
     A = inputs.uniform(g, (M, K))
     B = inputs.uniform(g, (K, N))
@@ -665,6 +695,10 @@ def test_leading_dimension_past_32_bit_offsets():
     with pytest.raises(sg.SgemmError) as e:  # the race-triage form has no register-staged kernel
         sg.sgemm_run_variant("mfma_serial", M, N, K, big, lda, dB, N, dC, N)
     assert e.value.status == sg._C["SGEMM_ERR_TOO_LARGE"]
+    dC.fill_(float("nan"))
+    sg.sgemm_run_variant("mfma_16", M, N, K, big, lda, dB, N, dC, N)
+    torch.cuda.synchronize()
+    assert oracle.check(dC.cpu().numpy(), Cref, Sabs).ok
     nbytes = sg.sgemm_bf16x3_workspace_size(M, N, K)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     dC.fill_(float("nan"))
