@@ -6,9 +6,9 @@
 // every wave loads all of its operands straight from global memory into
 // registers before its first matrix instruction: one memory round trip, no
 // LDS staging and no barrier until the four partial sums are added.  The
-// LDS-staged kernel (mfma_dma.hpp) spends two barriers and an LDS round trip
-// per slice; on a product this small those, not the arithmetic, set the
-// time.  Each wave reads its own operands, so L2 traffic grows with the tile
+// LDS-staged kernel (mfma_dma.hpp) spends a workgroup barrier and an LDS
+// round trip per K slice; on a product this small those, not the
+// arithmetic, set the time.  Each wave reads its own operands, so L2 traffic grows with the tile
 // count times K, and the tile rule (mfma_kernels.hip) keeps this kernel to
 // products whose tiles read little.
 //
