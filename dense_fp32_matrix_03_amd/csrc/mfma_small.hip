@@ -8,9 +8,9 @@
 // LDS staging and no barrier until the four partial sums are added.  The
 // LDS-staged kernel (mfma_dma.hpp) spends a workgroup barrier and an LDS
 // round trip per K slice; on a product this small those, not the
-// arithmetic, set the time.  Each wave reads its own operands, so L2 traffic grows with the tile
-// count times K, and the tile rule (mfma_kernels.hip) keeps this kernel to
-// products whose tiles read little.
+// arithmetic, set the time.  Each wave reads its own operands, so L2
+// traffic grows with the tile count times K, and the tile rule
+// (mfma_kernels.hip) keeps this kernel to products whose tiles read little.
 //
 // k order.  K is walked in chunks of 64 NG values; in a chunk, group g (16
 // consecutive k) goes to wave g % 4, and within a group lane quarter h
