@@ -466,7 +466,8 @@ def general_table(settle: float) -> list[dict]:
 # rule; 1000 x 1500 x 777 is the ragged workload (A rows not 16-byte aligned).
 SMALL = ((256, 256, 256, 256), (300, 260, 100, 100), (128, 128, 128, 128), (256, 256, 32, 32),
          (768, 256, 256, 256), (256, 256, 1024, 1024), (512, 512, 64, 64), (512, 512, 128, 128),
-         (384, 384, 256, 256), (100, 3000, 64, 64), (640, 640, 128, 128), (512, 512, 256, 256),
+         (384, 384, 256, 256), (100, 3000, 64, 64), (640, 640, 64, 64), (640, 640, 128, 128),
+         (1000, 130, 256, 256), (512, 512, 256, 256),
          (384, 384, 512, 512), (1000, 130, 1024, 1024), (512, 512, 512, 512),
          (768, 768, 768, 768), (640, 640, 2048, 2048), (1000, 130, 2048, 2048),
          (768, 1024, 512, 512), (832, 1024, 512, 512), (1024, 1024, 1024, 1024),

@@ -54,8 +54,8 @@ enum class MfmaPath { Auto, Staged, Unpadded, Serial };
 // buffer-to-LDS tile that wastes the least matrix-core time to partly filled
 // rounds of work-groups and to tile area outside C, preferring the larger
 // tile when two come within 3% of each other -- unless small_product()
-// holds and either the 16 x 16 tiles read at most 64 KiB per compute unit
-// or that best tile keeps under 90% of the matrix-core time on C: then the
+// holds and either the 16 x 16 tiles read at most 56 KiB per compute unit
+// or that best tile keeps under half of the matrix-core time on C: then the
 // 16 x 16 tile.
 TileChoice choose_mfma_tile(long M, long N, long K, int cus, long batch = 1);
 

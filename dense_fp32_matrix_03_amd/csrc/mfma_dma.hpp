@@ -159,7 +159,8 @@ struct SliceGeom {
 // KSPLIT: the work-group runs KSPLIT sets of WM x WN waves over the same
 // tile; set q takes the k groups g with g % KSPLIT == q of every slice, and
 // the sets' partial sums are added in the order 0, 1, .., KSPLIT - 1 through
-// LDS at the end.  A small tile then keeps all four SIMDs of its CU busy,
+// LDS at the end, each set adding and storing its share of every block's
+// registers.  A small tile then keeps all four SIMDs of its CU busy,
 // which is what lets a product with fewer 64 x 64 tiles than CUs spread over
 // the whole chip; the order of additions is still fixed for a given call
 // shape.
@@ -246,9 +247,10 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     else if constexpr (i == 2) return Bs2;
     else return Bs3;
   };
-  // Partial sums of k sets 1 .. KSPLIT-1 for the final reduction.
+  // Partial sums that each k set hands to the others for the final
+  // reduction (one slot per set; a set's own registers stay unwritten).
   constexpr int kRedSlot = NWT * FM * FN * 16 * kWave;
-  __shared__ __attribute__((aligned(1024))) float Red[KSPLIT > 1 ? (KSPLIT - 1) * kRedSlot : 1];
+  __shared__ __attribute__((aligned(1024))) float Red[KSPLIT > 1 ? KSPLIT * kRedSlot : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -457,69 +459,124 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   __builtin_amdgcn_s_waitcnt(0x0f70);
   phase(2);
 
+  // Register e of each accumulator block belongs to k set e / EPS: that set
+  // adds the block's partial sums for it and stores it.  With one k set
+  // everything belongs to set 0.
+  static_assert(16 % KSPLIT == 0, "k sets must share the 16 registers of a block evenly");
+  constexpr int EPS = 16 / KSPLIT;
+  auto slot = [&](int q, int i, int j, int e) {
+    return ((((q * NWT + wl) * FM + i) * FN + j) * 16 + e) * kWave + lane;
+  };
   if constexpr (KSPLIT > 1) {
-    // k sets 1.. leave their sums in LDS; set 0 adds them in order and
-    // stores C.
-    if (kq > 0) {
-      float *red = Red + (kq - 1) * kRedSlot;
+    // Every set leaves in LDS the registers the other sets own; after the
+    // barrier each set adds, for its own registers, the sums of sets 0, 1,
+    // .., KSPLIT-1 in that order.  The additions and the stores of C are
+    // shared by all sets, and each element is the same sum, in the same
+    // order, as when one set adds up all of them.
+    static_for<KSPLIT>([&](auto Q) {
+      constexpr int q = decltype(Q)::value;
+      if (kq == q) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+          for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            red[(((wl * FM + i) * FN + j) * 16 + e) * kWave + lane] = acc[i][j][e];
-    }
+            for (int e = 0; e < 16; ++e)
+              if (e / EPS != q) Red[slot(q, i, j, e)] = acc[i][j][e];
+      }
+    });
     __syncthreads();
-    if (kq != 0) return;
+    static_for<KSPLIT>([&](auto Q) {
+      constexpr int q = decltype(Q)::value;
+      if (kq == q) {
 #pragma unroll
-    for (int q = 1; q < KSPLIT; ++q)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+          for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+            for (int ee = 0; ee < EPS; ++ee) {
+              const int e = q * EPS + ee;
+              float sum = q == 0 ? acc[i][j][e] : Red[slot(0, i, j, e)];
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            acc[i][j][e] += Red[(q - 1) * kRedSlot + (((wl * FM + i) * FN + j) * 16 + e) * kWave + lane];
+              for (int r = 1; r < KSPLIT; ++r) sum += r == q ? acc[i][j][e] : Red[slot(r, i, j, e)];
+              acc[i][j][e] = sum;
+            }
+      }
+    });
   }
 
   phase(3);
   // Epilogue: register e of lane l holds row acc32_row(l, e), column l % 32
   // of its 32x32 block; rows >= M and columns >= N are not stored.  C is read
-  // only when beta != 0, and then a block's 16 values per lane are all loaded
+  // only when beta != 0, and then a block's values per lane are all loaded
   // before any of them is stored (a store could alias a later load, so the
   // compiler would otherwise wait out each load's latency in turn).  Stores
   // that do not follow a read of C are non-temporal: C is not read again by
   // this kernel, and streaming it out instead of leaving it dirty in L2 took
-  // 2048^3 from 144.3 to 146.1 TFLOP/s (1024^3: 112.6 to 114.1).
+  // 2048^3 from 144.3 to 146.1 TFLOP/s (1024^3: 112.6 to 114.1).  Each k set
+  // stores the registers it owns.
   const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN + r32;
   const bool full = (m0 + BM <= p.M) && (n0 + BN <= p.N);
   const bool plain = p.alpha == 1.f && p.beta == 0.f;
+  if constexpr (KSPLIT == 1) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = col0 + j * 32;
-      auto row = [&](int e) { return row0 + i * 32 + acc32_row(lane, e); };
-      auto inside = [&](int e) { return full || (row(e) < p.M && col < p.N); };
-      auto at = [&](int e) { return Cb + (long)row(e) * p.ldc + col; };
-      if (plain) {
+      for (int j = 0; j < FN; ++j) {
+        const int col = col0 + j * 32;
+        auto row = [&](int e) { return row0 + i * 32 + acc32_row(lane, e); };
+        auto inside = [&](int e) { return full || (row(e) < p.M && col < p.N); };
+        auto at = [&](int e) { return Cb + (long)row(e) * p.ldc + col; };
+        if (plain) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (inside(e)) __builtin_nontemporal_store(acc[i][j][e], at(e));
-      } else if (p.beta == 0.f) {
+          for (int e = 0; e < 16; ++e)
+            if (inside(e)) __builtin_nontemporal_store(acc[i][j][e], at(e));
+        } else if (p.beta == 0.f) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (inside(e)) __builtin_nontemporal_store(p.alpha * acc[i][j][e], at(e));
-      } else {
-        float c[16];
+          for (int e = 0; e < 16; ++e)
+            if (inside(e)) __builtin_nontemporal_store(p.alpha * acc[i][j][e], at(e));
+        } else {
+          float c[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) c[e] = inside(e) ? *at(e) : 0.f;
+          for (int e = 0; e < 16; ++e) c[e] = inside(e) ? *at(e) : 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (inside(e)) *at(e) = fmaf(p.alpha, acc[i][j][e], p.beta * c[e]);
+          for (int e = 0; e < 16; ++e)
+            if (inside(e)) *at(e) = fmaf(p.alpha, acc[i][j][e], p.beta * c[e]);
+        }
       }
-    }
+  } else {
+    // Set q stores registers q EPS .. q EPS + EPS - 1 of each block.
+    static_for<KSPLIT>([&](auto Q) {
+      constexpr int e0 = decltype(Q)::value * EPS;
+      if (kq == decltype(Q)::value) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int col = col0 + j * 32;
+            auto row = [&](int e) { return row0 + i * 32 + acc32_row(lane, e); };
+            auto inside = [&](int e) { return full || (row(e) < p.M && col < p.N); };
+            auto at = [&](int e) { return Cb + (long)row(e) * p.ldc + col; };
+            if (plain) {
+#pragma unroll
+              for (int e = e0; e < e0 + EPS; ++e)
+                if (inside(e)) __builtin_nontemporal_store(acc[i][j][e], at(e));
+            } else if (p.beta == 0.f) {
+#pragma unroll
+              for (int e = e0; e < e0 + EPS; ++e)
+                if (inside(e)) __builtin_nontemporal_store(p.alpha * acc[i][j][e], at(e));
+            } else {
+              float c[EPS];
+#pragma unroll
+              for (int e = e0; e < e0 + EPS; ++e) c[e - e0] = inside(e) ? *at(e) : 0.f;
+#pragma unroll
+              for (int e = e0; e < e0 + EPS; ++e)
+                if (inside(e)) *at(e) = fmaf(p.alpha, acc[i][j][e], p.beta * c[e - e0]);
+            }
+          }
+      }
+    });
+  }
   if constexpr (PHASES) {
     __builtin_amdgcn_s_waitcnt(0);
     phase(4);

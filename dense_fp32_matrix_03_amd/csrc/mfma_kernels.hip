@@ -102,14 +102,16 @@ TileChoice with_slice_rule(MfmaTile tile, long M, long N, long K, int cus, long 
 // 512^3 and 1000 x 130 x 2048 take 32 x 32; 256^3 16 x 16.
 //
 // The 16 x 16 small-product tile, measured on 256 CUs against the best
-// buffer-to-LDS tile (kernel trace): 256^3 5.49 -> 3.77 us, 256 x 256 x 1024
-// 8.22 -> 6.77, 512 x 512 x 64 4.80 -> 3.91, 512 x 512 x 128 5.36 -> 4.79,
-// 384 x 384 x 256 5.47 -> 5.14, 100 x 3000 x 64 5.31 -> 4.36.  It loses once
-// its tiles read more than 128 KiB per CU (384 x 384 x 512: 7.55 against
-// 6.61; 1000 x 130 x 1024: 16.62 against 10.16), and at 64-128 KiB per CU
-// against a buffer-to-LDS tile that fills the CUs (512 x 512 x 256: 6.08
-// against 5.65).  Shapes with more than 8 of its tiles per CU were not
-// measured.
+// buffer-to-LDS tile (kernel trace): 256^3 4.88 -> 3.79 us, 256 x 256 x 1024
+// 8.07 -> 6.71, 128^3 4.29 -> 3.09, 512 x 512 x 64 4.25 -> 3.93, 100 x 3000
+// x 64 4.83 -> 4.55 (its tiles read 4-50 KiB per CU, or 128 KiB where the
+// 32 x 32 tile fills a quarter of the CUs).  Where its tiles read 64-100 KiB
+// per CU and a buffer-to-LDS tile keeps at least half the matrix-core time
+// on C it loses (384 x 384 x 256: 5.29 against 5.01; 768 x 256 x 256: 5.26
+// against 5.02; 512 x 512 x 128: 4.79 against 4.66; 640 x 640 x 128: 5.73
+// against 5.22), and past 128 KiB per CU it loses by more (384 x 384 x 512:
+// 7.50 against 6.07; 1000 x 130 x 1024: 16.50 against 9.41).  Shapes with
+// more than 8 of its tiles per CU were not measured.
 TileChoice choose_mfma_tile(long M, long N, long K, int cus, long batch) {
   auto eff = [&](const TileShape &t) {
     return t.tile == MfmaTile::T16 ? 0.0 : tile_efficiency(t, M, N, cus, batch);
@@ -117,7 +119,7 @@ TileChoice choose_mfma_tile(long M, long N, long K, int cus, long batch) {
   double best = 0.0;
   for (const TileShape &t : kTileShapes) best = fmax(best, eff(t));
   if (small_product(M, N, K, cus, batch) &&
-      (small_bytes_per_cu(M, N, K, cus, batch) <= 64.0 * 1024 || best < 0.9))
+      (small_bytes_per_cu(M, N, K, cus, batch) <= 56.0 * 1024 || best < 0.5))
     return with_slice_rule(MfmaTile::T16, M, N, K, cus, batch);
   for (const TileShape &t : kTileShapes)
     if (best > 0.0 && eff(t) >= 0.97 * best) return with_slice_rule(t.tile, M, N, K, cus, batch);

@@ -88,8 +88,8 @@ extern "C" {
  * within 3%.  A product with K <= 1024, at most 8 tiles of 16 x 16 per
  * compute unit and at most 128 KiB of operand reads per compute unit on
  * those tiles (128 K bytes per tile) takes the 16 x 16 tile instead when
- * those reads stay within 64 KiB per compute unit or the best of the other
- * tiles would spend under 90% of the matrix-core time on C.  The _MFMA_<n> variants force a tile instead (with the same rule
+ * those reads stay within 56 KiB per compute unit or the best of the other
+ * tiles would spend under half of the matrix-core time on C.  The _MFMA_<n> variants force a tile instead (with the same rule
  * for its form): the 64 x 64 tile runs four waves, or two sets of four when
  * its work-groups fit one round on the compute units and K >= 512; the
  * 32 x 64 tile two sets of two waves and the 32 x 32 tile four single waves,

@@ -370,8 +370,8 @@ def _expected_tile(M, N, K, batch, cus):
         return float(M) * N * batch / (rounds * cus * bm * bn)
     best = max(eff(*t) for t in TILE_RULE)
     tiles16 = -(-M // 16) * -(-N // 16) * batch
-    if _small_product(M, N, K, batch, cus) and (tiles16 * K * 128 <= 64 * 1024 * cus
-                                                 or best < 0.9):
+    if _small_product(M, N, K, batch, cus) and (tiles16 * K * 128 <= 56 * 1024 * cus
+                                                 or best < 0.5):
         return "mfma_16"
     for t in TILE_RULE:
         if eff(*t) >= 0.97 * best:
@@ -383,9 +383,10 @@ def test_expected_tile_on_256_cus():
     """The restated rule on 256 CUs picks the tiles measured best."""
     assert _expected_tile(256, 256, 256, 1, 256) == "mfma_16"
     assert _expected_tile(300, 260, 100, 1, 256) == "mfma_16"
-    assert _expected_tile(768, 256, 256, 1, 256) == "mfma_16"
+    assert _expected_tile(768, 256, 256, 1, 256) == "mfma_32"    # 96 KiB per CU, 32 x 32 fills 3/4
     assert _expected_tile(512, 512, 64, 1, 256) == "mfma_16"
-    assert _expected_tile(512, 512, 128, 1, 256) == "mfma_16"    # 64 KiB per CU
+    assert _expected_tile(512, 512, 128, 1, 256) == "mfma_32"    # 64 KiB per CU
+    assert _expected_tile(100, 3000, 64, 1, 256) == "mfma_16"    # 41 KiB per CU
     assert _expected_tile(512, 512, 256, 1, 256) == "mfma_32"    # 128 KiB, 32 x 32 fills the CUs
     assert _expected_tile(256, 256, 1024, 1, 256) == "mfma_16"   # at the traffic bound
     assert _expected_tile(384, 384, 512, 1, 256) == "mfma_32"    # over it
