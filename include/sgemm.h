@@ -82,21 +82,22 @@ extern "C" {
  * the operand is 16-byte aligned with a leading dimension and width that are
  * multiples of 4, else 4 bytes; only an operand whose leading dimension puts
  * one slice beyond 2 GiB is fetched through registers instead.  sgemm_run
- * picks the block tile (256 x 256, 128 x 128, 64 x 64, 32 x 64, 32 x 32 or
- * 16 x 16) that loses the least matrix-core time to partly filled rounds of
+ * picks the block tile (256 x 256, 128 x 128, 64 x 64, 32 x 64 or 32 x 32)
+ * that loses the least matrix-core time to partly filled rounds of
  * work-groups and to tile area outside C, the larger one when two come
  * within 3%.  A product with K <= 1024, at most 8 tiles of 16 x 16 per
  * compute unit and at most 128 KiB of operand reads per compute unit on
  * those tiles (128 K bytes per tile) takes the 16 x 16 tile instead when
  * those reads stay within 56 KiB per compute unit or the best of the other
- * tiles would spend under half of the matrix-core time on C.  The _MFMA_<n> variants force a tile instead (with the same rule
- * for its form): the 64 x 64 tile runs four waves, or two sets of four when
- * its work-groups fit one round on the compute units and K >= 512; the
- * 32 x 64 tile two sets of two waves and the 32 x 32 tile four single waves,
- * each set summing its share of every K slice; the 16 x 16 tile (the
- * 16x16x4 matrix instruction) four single waves that load their share of K
- * straight from global memory into registers, with no LDS staging; the
- * sets' partial sums are added in a fixed order.  SGEMM_VARIANT_MFMA_STAGED always fetches through
+ * tiles would spend under half of the matrix-core time on C.  The
+ * _MFMA_<n> variants force a tile (with the same rule for its form): the
+ * 64 x 64 tile runs four waves, or two sets of four when its work-groups fit
+ * one round on the compute units and K >= 512; the 32 x 64 tile two sets of
+ * two waves and the 32 x 32 tile four single waves, each set summing its
+ * share of every K slice; the 16 x 16 tile (the 16x16x4 matrix instruction)
+ * four single waves that load their share of K straight from global memory
+ * into registers, with no LDS staging.  The sets' partial sums are added in
+ * a fixed order.  SGEMM_VARIANT_MFMA_STAGED always fetches through
  * registers, SGEMM_VARIANT_MFMA_UNPADDED drops the LDS anti-conflict
  * layout (the chapter's padding, section 三), and SGEMM_VARIANT_MFMA_DWORD
  * fetches both operands 4 bytes per lane even where 16-byte loads are
