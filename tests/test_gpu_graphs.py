@@ -37,10 +37,12 @@ def _replays_match(capture_body, out, eager_bits, replays=5):
         assert out.cpu().numpy().tobytes() == eager_bits, f"replay {r}"
 
 
-def test_sgemm_run_and_general_form_in_a_graph():
+# 520 x 384 x 260 runs the buffer-to-LDS kernel (32 x 32 tile, four k sets);
+# 256 x 256 x 256 the 16 x 16 small-product kernel.
+@pytest.mark.parametrize("M,N,K", [(520, 384, 260), (256, 256, 256)])
+def test_sgemm_run_and_general_form_in_a_graph(M, N, K):
     import torch
-    g0 = np.random.default_rng(61)
-    M, N, K = 520, 384, 260
+    g0 = np.random.default_rng(61 + M)
     dA = torch.from_numpy(inputs.uniform(g0, (M, K))).cuda()
     dBt = torch.from_numpy(inputs.uniform(g0, (N, K))).cuda()
     dB = dBt.t().contiguous()
