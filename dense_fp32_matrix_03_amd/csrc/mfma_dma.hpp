@@ -518,6 +518,9 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN + r32;
   const bool full = (m0 + BM <= p.M) && (n0 + BN <= p.N);
   const bool plain = p.alpha == 1.f && p.beta == 0.f;
+  // The one-set form is written out on its own: folded into the per-set
+  // form below, the compiler stops specialising the stores on `full`, and
+  // the 128 x 128 kernel grows from about 2500 to 3800 instructions.
   if constexpr (KSPLIT == 1) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
