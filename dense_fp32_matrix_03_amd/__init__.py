@@ -87,6 +87,9 @@ def load_library(path: str = LIB_PATH):
     lib.sgemm_mfma_ceiling.restype = ci
     lib.sgemm_phase_times.argtypes = gemm_args[:-1] + [vp, i64, ctypes.POINTER(i64), vp]
     lib.sgemm_phase_times.restype = ci
+    pi = ctypes.POINTER(ci)
+    lib.sgemm_tile_choice.argtypes = [i64, i64, i64, i64, ci, pi, pi, pi, pi]
+    lib.sgemm_tile_choice.restype = ci
     lib.sgemm_mfma_probe.argtypes = [ci, vp, vp, vp, vp]
     lib.sgemm_mfma_probe.restype = ci
     lib.sgemm_status_string.argtypes = [ci]
@@ -150,6 +153,15 @@ def sgemm_run_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
     _check("sgemm_run_ex", load_library().sgemm_run_ex(
         int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
         float(beta), _ptr(C), ldc, _stream(stream)))
+
+
+def sgemm_tile_choice(M, N, K, batch=1, cus=256) -> tuple:
+    """(bm, bn, bk, ksets) that sgemm_run and the general form choose for
+    `batch` products of M x N x K on `cus` compute units (host logic only)."""
+    out = [ctypes.c_int() for _ in range(4)]
+    _check("sgemm_tile_choice", load_library().sgemm_tile_choice(
+        M, N, K, batch, cus, *(ctypes.byref(o) for o in out)))
+    return tuple(o.value for o in out)
 
 
 def sgemm_run_strided_batched(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb,

@@ -213,6 +213,21 @@ int sgemm_run(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
   return sgemm_run_variant(SGEMM_VARIANT_MFMA, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
+int sgemm_tile_choice(int64_t M, int64_t N, int64_t K, int64_t batch, int cus, int *bm, int *bn,
+                      int *bk, int *ksets) {
+  if (M < 1 || N < 1 || K < 1 || batch < 1 || cus < 1) return SGEMM_ERR_INVALID_VALUE;
+  if (!bm || !bn || !bk || !ksets) return SGEMM_ERR_INVALID_VALUE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim || batch > kMaxDim) return SGEMM_ERR_TOO_LARGE;
+  if (!grid_fits(M, N, batch, 64, 64, 256)) return SGEMM_ERR_TOO_LARGE;
+  const sgemm::TileChoice t = sgemm::choose_mfma_tile(M, N, K, cus, batch);
+  const sgemm::TileGeometry g = sgemm::tile_geometry(t, true, K);
+  *bm = g.bm;
+  *bn = g.bn;
+  *bk = g.bk;
+  *ksets = g.ksets;
+  return SGEMM_OK;
+}
+
 int sgemm_phase_times(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
                       const float *B, int64_t ldb, float *C, int64_t ldc, uint64_t *times,
                       int64_t times_len, int64_t *workgroups, void *stream) {

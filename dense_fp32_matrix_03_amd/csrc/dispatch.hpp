@@ -68,6 +68,14 @@ bool small_product(long M, long N, long K, int cus, long batch = 1);
 // `tile` with the K-slice length choose_mfma_tile would give it.
 TileChoice with_slice_rule(MfmaTile tile, long M, long N, long K, int cus, long batch = 1);
 
+// What a tile choice launches for the plain layout (wide: both operands take
+// 16-byte loads): block tile bm x bn, K slice bk (for the 16 x 16 tile, the K
+// one pass of its four waves covers) and the number of k sets.
+struct TileGeometry {
+  int bm, bn, bk, ksets;
+};
+TileGeometry tile_geometry(TileChoice tile, bool wide, long K);
+
 // Matrix-core product.  va / vb: A / B qualify for 128-bit loads.
 hipError_t launch_mfma(TileChoice tile, MfmaPath path, const GemmArgs &p, bool va, bool vb,
                        hipStream_t stream);

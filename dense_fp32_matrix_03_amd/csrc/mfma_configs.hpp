@@ -24,23 +24,24 @@ namespace sgemm {
 //   C32L      the same with 64-float K slices
 enum class DmaCfg { C256, C128, C64, C64K2, C64K2L, C32x64, C32x64L, C32, C32L };
 
+// Block tile, K slice and k sets (the KSPLIT of launch_dma_layout below).
 struct DmaGeom {
-  int bm, bn, bk;
+  int bm, bn, bk, ksets;
 };
 
 inline DmaGeom dma_geom(DmaCfg c) {
   switch (c) {
-    case DmaCfg::C256: return {256, 256, 32};
-    case DmaCfg::C128: return {128, 128, 32};
-    case DmaCfg::C64: return {64, 64, 32};
-    case DmaCfg::C64K2: return {64, 64, 32};
-    case DmaCfg::C64K2L: return {64, 64, 64};
-    case DmaCfg::C32x64: return {32, 64, 32};
-    case DmaCfg::C32x64L: return {32, 64, 64};
-    case DmaCfg::C32: return {32, 32, 32};
-    case DmaCfg::C32L: return {32, 32, 64};
+    case DmaCfg::C256: return {256, 256, 32, 1};
+    case DmaCfg::C128: return {128, 128, 32, 1};
+    case DmaCfg::C64: return {64, 64, 32, 1};
+    case DmaCfg::C64K2: return {64, 64, 32, 2};
+    case DmaCfg::C64K2L: return {64, 64, 64, 2};
+    case DmaCfg::C32x64: return {32, 64, 32, 2};
+    case DmaCfg::C32x64L: return {32, 64, 64, 2};
+    case DmaCfg::C32: return {32, 32, 32, 4};
+    case DmaCfg::C32L: return {32, 32, 64, 4};
   }
-  return {0, 0, 0};
+  return {0, 0, 0, 0};
 }
 
 // Launch configuration c for operand layout (TA, TB); SWZ = false drops the

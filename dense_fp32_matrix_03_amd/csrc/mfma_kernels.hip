@@ -126,6 +126,16 @@ TileChoice choose_mfma_tile(long M, long N, long K, int cus, long batch) {
   return with_slice_rule(MfmaTile::T128, M, N, K, cus, batch);
 }
 
+TileGeometry tile_geometry(TileChoice tile, bool wide, long K) {
+  if (tile.tile == MfmaTile::T16) {
+    int ng = 1;  // groups of 16 k per wave and pass, as mfma_small.hip picks them
+    while (ng < 16 && 64L * ng < K) ng *= 2;
+    return {16, 16, 64 * ng, 4};
+  }
+  const DmaGeom g = dma_geom(dma_cfg(tile, wide));
+  return {g.bm, g.bn, g.bk, g.ksets};
+}
+
 hipError_t launch_mfma(TileChoice tile, MfmaPath path, const GemmArgs &p, bool va, bool vb,
                        hipStream_t stream) {
   if (path == MfmaPath::Staged) return launch_staged(tile.tile, true, p, va, vb, stream);

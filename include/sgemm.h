@@ -262,6 +262,20 @@ int sgemm_phase_times(int64_t M, int64_t N, int64_t K, const float *A, int64_t l
                       const float *B, int64_t ldb, float *C, int64_t ldc, uint64_t *times,
                       int64_t times_len, int64_t *workgroups, void *stream);
 
+/*
+ * The matrix-core configuration that sgemm_run (batch = 1) and the general
+ * form choose for `batch` products of M x N x K on a device with `cus`
+ * compute units, for the plain layout with 16-byte loads on both operands
+ * (the rule is described with the variants above).  Host logic only: no
+ * device call, and no sgemm_create needed.  Writes the block tile
+ * (*bm x *bn), the K slice *bk (for the 16 x 16 tile, the K that one pass
+ * of its four waves covers) and the number of k sets *ksets (host memory).
+ * SGEMM_ERR_INVALID_VALUE for M, N, K, batch or cus below 1 or a null
+ * pointer; SGEMM_ERR_TOO_LARGE past sgemm_run's limits.
+ */
+int sgemm_tile_choice(int64_t M, int64_t N, int64_t K, int64_t batch, int cus, int *bm, int *bn,
+                      int *bk, int *ksets);
+
 /* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
 const char *sgemm_status_string(int status);
 
