@@ -614,6 +614,16 @@ def phase_table(settle: float) -> list[dict]:
              "store_us": round(mean(q[:, 4] - q[:, 3]), 3),
              "workgroup_us": round(mean(q[:, 4] - q[:, 0]), 3),
              "clock_mhz": round(clock, 0), "loop_mfma_us": round(loop_mfma_us, 3)}
+        # Work-group w runs on XCD w % 8 (the dispatcher deals work-groups
+        # to the eight XCDs in turn): per-XCD shader clock, main loop in
+        # cycles at that clock, and the last end of a work-group.
+        xcd = np.arange(wgs) % 8
+        wg_clock = (q[:, 6] - q[:, 5]) / np.maximum(q[:, 4] - q[:, 0], 1) * REALTIME_MHZ
+        loop_cyc = (q[:, 2] - q[:, 1]) * us * wg_clock
+        xs = [x for x in range(8) if (xcd == x).any()]
+        r["xcd_clock_mhz"] = [round(float(wg_clock[xcd == x].mean()), 0) for x in xs]
+        r["xcd_loop_kcycles"] = [round(float(loop_cyc[xcd == x].mean()) / 1e3, 2) for x in xs]
+        r["xcd_end_us"] = [round(float(q[xcd == x, 4].max() - q[:, 0].min()) * us, 2) for x in xs]
         print(json.dumps(r), flush=True)
         rows.append(r)
         del dA, dB, dC, t
