@@ -488,12 +488,17 @@ def test_race_triage_schedule_gives_the_same_bits(M, N, K, lda):
 # -- the phase-timestamp diagnostic ----------------------------------------------------
 
 @pytest.mark.parametrize("M,N,K,lda", [(256, 256, 256, 256), (1000, 1500, 777, 777),
-                                       (1024, 1024, 2048, 2048), (2048, 2048, 96, 96)])
+                                       (1024, 1024, 2048, 2048), (2048, 2048, 96, 96),
+                                       (100, 3000, 64, 64), (512, 512, 512, 512),
+                                       (640, 640, 2048, 2048), (3072, 3072, 1024, 1024),
+                                       (1024, 1024, 1024, 1024)])
 def test_phase_times_diagnostic(M, N, K, lda):
     """sgemm_phase_times computes sgemm_run's bits (same tile and kernel
     code), and each work-group's timestamps are in order (start <= first
     slice landed <= last slice computed <= k sets reduced <= stores
-    complete), with a tile record whose block count matches the launch."""
+    complete), with a tile record whose block count matches the launch and
+    whose tile, K slice and k sets are what sgemm_tile_choice reports for
+    this device's CU count."""
     import torch
     g = np.random.default_rng(M + N + K)
     A = inputs.padded(inputs.uniform(g, (M, K)), lda)
@@ -517,6 +522,8 @@ def test_phase_times_diagnostic(M, N, K, lda):
     assert np.all(q[:, 7] == tile)
     bm, bn, bk, ks = tile & 0xffff, (tile >> 16) & 0xffff, (tile >> 32) & 0xffff, tile >> 48
     assert -(-M // bm) * -(-N // bn) == wgs and bk % 16 == 0 and ks in (1, 2, 4)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert (bm, bn, bk, ks) == sg.sgemm_tile_choice(M, N, K, 1, cus)
 
 
 # -- degenerate sizes and errors --------------------------------------------------------
