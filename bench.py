@@ -471,9 +471,12 @@ SMALL = ((256, 256, 256, 256), (300, 260, 100, 100), (128, 128, 128, 128), (256,
          (384, 384, 512, 512), (1000, 130, 1024, 1024), (512, 512, 512, 512),
          (768, 768, 768, 768), (640, 640, 2048, 2048), (1000, 130, 2048, 2048),
          (768, 1024, 512, 512), (832, 1024, 512, 512), (1024, 1024, 1024, 1024),
-         (1000, 1500, 776, 776), (1000, 1500, 777, 777), (1536, 1536, 1536, 1536),
+         (1000, 1500, 776, 776), (1000, 1500, 777, 777), (960, 1600, 777, 777),
+         (1000, 1700, 777, 777), (1024, 1536, 1024, 1024), (1200, 1200, 1200, 1200),
+         (1536, 1536, 1536, 1536),
          (2048, 2048, 2048, 2048), (3072, 3072, 1024, 1024), (4096, 4096, 1024, 1024))
-SMALL_TILES = ("mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_32x64", "mfma_32", "mfma_16")
+SMALL_TILES = ("mfma", "mfma_256", "mfma_128", "mfma_64x96", "mfma_64", "mfma_32x64", "mfma_32",
+               "mfma_16")
 
 
 def small_table(steps: int, settle: float) -> list[dict]:

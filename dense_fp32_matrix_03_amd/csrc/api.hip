@@ -121,9 +121,12 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
   int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc);
   if (rc != SGEMM_OK) return rc;
   if (variant <= SGEMM_VARIANT_DBUF && !grid_fits(M, N, 1, 16, 16, 256)) return SGEMM_ERR_TOO_LARGE;
-  // Forced tiles: 512 threads per 64 x 64 block, 256 per 32 x 64, 32 x 32 or
-  // 16 x 16 block (sgemm_run only picks a tile whose launch fits).
+  // Forced tiles: 512 threads per 64 x 64 block, 768 per 64 x 96, 256 per
+  // 32 x 64, 32 x 32 or 16 x 16 block (sgemm_run only picks a tile whose
+  // launch fits).
   if (variant == SGEMM_VARIANT_MFMA_64 && !grid_fits(M, N, 1, 64, 64, 512))
+    return SGEMM_ERR_TOO_LARGE;
+  if (variant == SGEMM_VARIANT_MFMA_64X96 && !grid_fits(M, N, 1, 64, 96, 768))
     return SGEMM_ERR_TOO_LARGE;
   if (variant == SGEMM_VARIANT_MFMA_32X64 && !grid_fits(M, N, 1, 32, 64, 256))
     return SGEMM_ERR_TOO_LARGE;
@@ -176,6 +179,9 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
         break;
       case SGEMM_VARIANT_MFMA_64:
         err = sgemm::launch_mfma(forced(MfmaTile::T64), MfmaPath::Auto, p, va, vb, s);
+        break;
+      case SGEMM_VARIANT_MFMA_64X96:
+        err = sgemm::launch_mfma(forced(MfmaTile::T64x96), MfmaPath::Auto, p, va, vb, s);
         break;
       case SGEMM_VARIANT_MFMA_32X64:
         err = sgemm::launch_mfma(forced(MfmaTile::T32x64), MfmaPath::Auto, p, va, vb, s);
@@ -508,6 +514,7 @@ const char *sgemm_variant_name(int variant) {
     case SGEMM_VARIANT_MFMA_32X64: return "mfma_32x64_ksplit2";
     case SGEMM_VARIANT_MFMA_SERIAL: return "mfma_serial_race_triage";
     case SGEMM_VARIANT_MFMA_16: return "mfma_16x16_ksplit4";
+    case SGEMM_VARIANT_MFMA_64X96: return "mfma_64x96_ksplit2";
     default: return nullptr;
   }
 }

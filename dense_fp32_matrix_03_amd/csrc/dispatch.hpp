@@ -8,11 +8,11 @@
 namespace sgemm {
 
 // Block tiles of the matrix-core kernels (mfma_configs.hpp gives the wave
-// grids of the buffer-to-LDS kernel): 256 x 256, 128 x 128, 64 x 64, 32 x 64
-// (K split over two sets of waves) and 32 x 32 (four k sets); and 16 x 16,
-// the small-product kernel (mfma_small.hip: four k sets of one wave, operands
-// loaded straight into registers).
-enum class MfmaTile { T256, T128, T64, T32x64, T32, T16 };
+// grids of the buffer-to-LDS kernel): 256 x 256, 128 x 128, 64 x 96 (K split
+// over two sets of six waves), 64 x 64, 32 x 64 (two k sets) and 32 x 32
+// (four k sets); and 16 x 16, the small-product kernel (mfma_small.hip: four
+// k sets of one wave, operands loaded straight into registers).
+enum class MfmaTile { T256, T128, T64x96, T64, T32x64, T32, T16 };
 
 // A tile and its form.  long_k selects 64-float K slices; ksplit (64 x 64
 // only) runs the tile with two k sets of four waves.
@@ -27,6 +27,7 @@ enum class MfmaTile { T256, T128, T64, T32x64, T32, T16 };
 //    Otherwise the four-wave form: with several work-groups per CU, or few
 //    K slices, the eight-wave form loses (1024 products of 64^3: 9.8 against
 //    16.2 us; 3072 x 3072 x 1024: 136.8 against 139.6 us).
+//  - The 64 x 96 tile has one form: 32-float slices, two k sets of six waves.
 //  - The 16 x 16 tile has no K slices; where a variant runs the
 //    buffer-to-LDS kernel instead, it takes the 32 x 32 tile's form.
 struct TileChoice {
@@ -53,10 +54,11 @@ enum class MfmaPath { Auto, Staged, Unpadded, Serial };
 // The tile for `batch` products of M x N x K on `cus` compute units: the
 // buffer-to-LDS tile that wastes the least matrix-core time to partly filled
 // rounds of work-groups and to tile area outside C, preferring the larger
-// tile when two come within 3% of each other -- unless small_product()
-// holds and either the 16 x 16 tiles read at most 56 KiB per compute unit
-// or that best tile keeps under half of the matrix-core time on C: then the
-// 16 x 16 tile.
+// tile when two come within 3% of each other, and the 64 x 96 tile only
+// where its work-groups fit one round on the compute units -- unless
+// small_product() holds and either the 16 x 16 tiles read at most 56 KiB per
+// compute unit or that best tile keeps under half of the matrix-core time on
+// C: then the 16 x 16 tile.
 TileChoice choose_mfma_tile(long M, long N, long K, int cus, long batch = 1);
 
 // Whether the 16 x 16 small-product kernel serves the product: K <= 1024,

@@ -18,11 +18,12 @@ namespace sgemm {
 //   C64       64 x  64 x 32, 2 x 2 waves of  32 x 32 (4 waves)
 //   C64K2     the same with two k sets (8 waves)
 //   C64K2L    C64K2 with 64-float K slices
+//   C64x96    64 x  96 x 32, 2 x 3 waves of  32 x 32, two k sets (12 waves)
 //   C32x64    32 x  64 x 32, 1 x 2 waves of  32 x 32, two k sets (4 waves)
 //   C32x64L   the same with 64-float K slices
 //   C32       32 x  32 x 32, one wave, four k sets (4 waves)
 //   C32L      the same with 64-float K slices
-enum class DmaCfg { C256, C128, C64, C64K2, C64K2L, C32x64, C32x64L, C32, C32L };
+enum class DmaCfg { C256, C128, C64, C64K2, C64K2L, C64x96, C32x64, C32x64L, C32, C32L };
 
 // Block tile, K slice and k sets (the KSPLIT of launch_dma_layout below).
 struct DmaGeom {
@@ -36,6 +37,7 @@ inline DmaGeom dma_geom(DmaCfg c) {
     case DmaCfg::C64: return {64, 64, 32, 1};
     case DmaCfg::C64K2: return {64, 64, 32, 2};
     case DmaCfg::C64K2L: return {64, 64, 64, 2};
+    case DmaCfg::C64x96: return {64, 96, 32, 2};
     case DmaCfg::C32x64: return {32, 64, 32, 2};
     case DmaCfg::C32x64L: return {32, 64, 64, 2};
     case DmaCfg::C32: return {32, 32, 32, 4};
@@ -79,6 +81,10 @@ hipError_t launch_dma_layout(DmaCfg c, const GemmArgs &p, bool va, bool vb, hipS
       break;
     case DmaCfg::C64K2L:
       launch_dma_widths<64, 64, 64, 2, 2, SWZ, SCHED, TA, TB, 2, 2,
+                        PHASES>(p, va, vb, s, kGroupM);
+      break;
+    case DmaCfg::C64x96:
+      launch_dma_widths<64, 96, 32, 2, 3, SWZ, SCHED, TA, TB, 2, 2,
                         PHASES>(p, va, vb, s, kGroupM);
       break;
     case DmaCfg::C32x64:

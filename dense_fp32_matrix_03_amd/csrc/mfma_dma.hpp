@@ -135,8 +135,13 @@ struct SliceGeom {
   static constexpr int E = WIDE ? 4 : 1;    // floats per lane per load
   static constexpr int FPB = kWave * E;     // floats per wave-wide load
   static constexpr int NB = R * W / FPB;    // loads per slice
-  static_assert(NB % NW == 0, "loads must split evenly over the waves");
-  static constexpr int NBW = NB / NW;       // loads per wave per slice
+  static_assert(R * W % FPB == 0, "a slice is a whole number of wave-wide loads");
+  static constexpr int NBW = (NB + NW - 1) / NW;  // loads per wave per slice
+  // Where the loads do not split evenly over the waves (the 12-wave 64 x 96
+  // tile), the last load of some waves is spare: it reads out of range (no
+  // memory traffic) into a dump area of LDS, so that every wave issues the
+  // same number of loads and the load counters of the barriers hold.
+  static constexpr bool SPARE = NB % NW != 0;
   static constexpr bool KR = KROWS;
 
   // Stored (row, col) of the window element that lane `lane` fetches in the
@@ -251,6 +256,8 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   // reduction (one slot per set; a set's own registers stay unwritten).
   constexpr int kRedSlot = NWT * FM * FN * 16 * kWave;
   __shared__ __attribute__((aligned(1024))) float Red[KSPLIT > 1 ? KSPLIT * kRedSlot : 1];
+  // Landing area of the spare loads (zeros, never read).
+  __shared__ __attribute__((aligned(1024))) float Dump[GA::SPARE || GB::SPARE ? 4 * kWave : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -282,6 +289,7 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     int row, col;
     GA::elem(wave, lane, q, row, col);
     offA[q] = m0 + GA::mnof(row, col) < p.M ? (unsigned)(row * p.lda + col) * 4u : kOutOfRange;
+    if constexpr (GA::SPARE) offA[q] = wave + q * NW < GA::NB ? offA[q] : kOutOfRange;
     kofA[q] = GA::kof(row, col);
   }
 #pragma unroll
@@ -289,6 +297,7 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     int row, col;
     GB::elem(wave, lane, q, row, col);
     offB[q] = n0 + GB::mnof(row, col) < p.N ? (unsigned)(row * p.ldb + col) * 4u : kOutOfRange;
+    if constexpr (GB::SPARE) offB[q] = wave + q * NW < GB::NB ? offB[q] : kOutOfRange;
     kofB[q] = GB::kof(row, col);
   }
 
@@ -319,13 +328,17 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     for (int q = 0; q < GA::NBW; ++q) {
       unsigned off = offA[q];
       if constexpr (!KFULL && !GA::KR) off = kofA[q] < kl ? off : kOutOfRange;
-      lds_dma<VA>(ra, as + (wave + q * NW) * GA::FPB, off);
+      float *dst = as + (wave + q * NW) * GA::FPB;
+      if constexpr (GA::SPARE) dst = wave + q * NW < GA::NB ? dst : Dump;
+      lds_dma<VA>(ra, dst, off);
     }
 #pragma unroll
     for (int q = 0; q < GB::NBW; ++q) {
       unsigned off = offB[q];
       if constexpr (!KFULL && !GB::KR) off = kofB[q] < kl ? off : kOutOfRange;
-      lds_dma<VB>(rb, bs + (wave + q * NW) * GB::FPB, off);
+      float *dst = bs + (wave + q * NW) * GB::FPB;
+      if constexpr (GB::SPARE) dst = wave + q * NW < GB::NB ? dst : Dump;
+      lds_dma<VB>(rb, dst, off);
     }
   };
 

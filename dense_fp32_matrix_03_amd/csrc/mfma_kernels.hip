@@ -21,6 +21,7 @@ struct TileShape {
 // per flop, more L2 reuse).
 constexpr TileShape kTileShapes[] = {{MfmaTile::T256, 256, 256, 512},
                                      {MfmaTile::T128, 128, 128, 512},
+                                     {MfmaTile::T64x96, 64, 96, 768},
                                      {MfmaTile::T64, 64, 64, 512},
                                      {MfmaTile::T32x64, 32, 64, 256},
                                      {MfmaTile::T32, 32, 32, 256},
@@ -51,6 +52,7 @@ DmaCfg dma_cfg(TileChoice t, bool wide_plain) {
   switch (t.tile) {
     case MfmaTile::T256: return wide_plain ? DmaCfg::C256 : DmaCfg::C128;
     case MfmaTile::T128: return DmaCfg::C128;
+    case MfmaTile::T64x96: return DmaCfg::C64x96;
     case MfmaTile::T64:
       return !t.ksplit ? DmaCfg::C64 : (t.long_k ? DmaCfg::C64K2L : DmaCfg::C64K2);
     case MfmaTile::T32x64: return t.long_k ? DmaCfg::C32x64L : DmaCfg::C32x64;
@@ -96,7 +98,8 @@ TileChoice with_slice_rule(MfmaTile tile, long M, long N, long K, int cus, long 
 }
 
 // Measured on 256 CUs (kernel trace and HIP events): 1000 x 1500 x 777
-// takes 32 x 64 (768 tiles, three full rounds: 31.9 -> 25.4 us against
+// takes 64 x 96 (256 tiles, one 12-wave work-group per CU: 24.9 us, against
+// 25.4 for 32 x 64 -- 768 tiles, three work-groups per CU -- and 31.9 for
 // 64 x 64, whose 384 tiles leave half the CUs idle in the second round);
 // 1024^3 takes 64 x 64 (256 tiles); 2048^3 128 x 128; 8192^3 256 x 256;
 // 512^3 and 1000 x 130 x 2048 take 32 x 32; 256^3 16 x 16.
@@ -114,7 +117,11 @@ TileChoice with_slice_rule(MfmaTile tile, long M, long N, long K, int cus, long 
 // more than 8 of its tiles per CU were not measured.
 TileChoice choose_mfma_tile(long M, long N, long K, int cus, long batch) {
   auto eff = [&](const TileShape &t) {
-    return t.tile == MfmaTile::T16 ? 0.0 : tile_efficiency(t, M, N, cus, batch);
+    if (t.tile == MfmaTile::T16) return 0.0;
+    // One 64 x 96 work-group (12 waves) fills a CU, so a second round could
+    // not overlap the first one's slices: one round only.
+    if (t.tile == MfmaTile::T64x96 && tile_count(M, N, t.bm, t.bn, batch) > cus) return 0.0;
+    return tile_efficiency(t, M, N, cus, batch);
   };
   double best = 0.0;
   for (const TileShape &t : kTileShapes) best = fmax(best, eff(t));

@@ -1,8 +1,8 @@
 // mfma_staged.hip -- the register-staged matrix-core kernel (mfma_gemm.hpp):
 // the ablation SGEMM_VARIANT_MFMA_STAGED, and sgemm_run's fallback when a
 // leading dimension puts one K slice beyond a buffer descriptor's 32-bit
-// offsets.  It has no k split, so the 32 x 64 and 32 x 32 tiles run on its
-// 64 x 64 tile.
+// offsets.  It has no k split, so the 64 x 96, 32 x 64 and 32 x 32 tiles run
+// on its 64 x 64 tile.
 #include "dispatch.hpp"
 #include "mfma_gemm.hpp"
 

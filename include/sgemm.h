@@ -45,10 +45,10 @@
  * below 2^32 work-items.  sgemm_run and the general form take any product
  * with at most 2^24 blocks of 64 x 64 (counting every product of a batch)
  * and pick a tile whose launch fits; the forced tiles need 512 work-items
- * per 64 x 64 block (SGEMM_VARIANT_MFMA_64) or 256 per 32 x 64
- * (SGEMM_VARIANT_MFMA_32X64), 32 x 32 (SGEMM_VARIANT_MFMA_32) or 16 x 16
- * block (SGEMM_VARIANT_MFMA_16), the vector-FMA variants 256 per 16 x 16
- * block.
+ * per 64 x 64 block (SGEMM_VARIANT_MFMA_64), 768 per 64 x 96 block
+ * (SGEMM_VARIANT_MFMA_64X96) or 256 per 32 x 64 (SGEMM_VARIANT_MFMA_32X64),
+ * 32 x 32 (SGEMM_VARIANT_MFMA_32) or 16 x 16 block (SGEMM_VARIANT_MFMA_16),
+ * the vector-FMA variants 256 per 16 x 16 block.
  *
  * Threads.  sgemm_create / sgemm_destroy are serialised internally;
  * sgemm_run may be called from any thread once sgemm_create has succeeded.
@@ -82,19 +82,21 @@ extern "C" {
  * the operand is 16-byte aligned with a leading dimension and width that are
  * multiples of 4, else 4 bytes; only an operand whose leading dimension puts
  * one slice beyond 2 GiB is fetched through registers instead.  sgemm_run
- * picks the block tile (256 x 256, 128 x 128, 64 x 64, 32 x 64 or 32 x 32)
- * that loses the least matrix-core time to partly filled rounds of
+ * picks the block tile (256 x 256, 128 x 128, 64 x 96, 64 x 64, 32 x 64 or
+ * 32 x 32) that loses the least matrix-core time to partly filled rounds of
  * work-groups and to tile area outside C, the larger one when two come
- * within 3%.  A product with K <= 1024, at most 8 tiles of 16 x 16 per
+ * within 3%; the 64 x 96 tile only where its work-groups fit one round on
+ * the compute units.  A product with K <= 1024, at most 8 tiles of 16 x 16 per
  * compute unit and at most 128 KiB of operand reads per compute unit on
  * those tiles (128 K bytes per tile) takes the 16 x 16 tile instead when
  * those reads stay within 56 KiB per compute unit or the best of the other
  * tiles would spend under half of the matrix-core time on C.  The
  * _MFMA_<n> variants force a tile (with the same rule for its form): the
  * 64 x 64 tile runs four waves, or two sets of four when its work-groups fit
- * one round on the compute units and K >= 512; the 32 x 64 tile two sets of
- * two waves and the 32 x 32 tile four single waves, each set summing its
- * share of every K slice; the 16 x 16 tile (the 16x16x4 matrix instruction)
+ * one round on the compute units and K >= 512; the 64 x 96 tile two sets of
+ * six waves (one work-group fills a CU), the 32 x 64 tile two sets of two
+ * waves and the 32 x 32 tile four single waves, each set summing its share
+ * of every K slice; the 16 x 16 tile (the 16x16x4 matrix instruction)
  * four single waves that load their share of K straight from global memory
  * into registers, with no LDS staging.  The sets' partial sums are added in
  * a fixed order.  SGEMM_VARIANT_MFMA_STAGED always fetches through
@@ -130,7 +132,8 @@ extern "C" {
 #define SGEMM_VARIANT_MFMA_32X64 12
 #define SGEMM_VARIANT_MFMA_SERIAL 13
 #define SGEMM_VARIANT_MFMA_16 14
-#define SGEMM_NUM_VARIANTS 15
+#define SGEMM_VARIANT_MFMA_64X96 15
+#define SGEMM_NUM_VARIANTS 16
 
 /*
  * Initialise the library for the current device: checks that it is gfx950

@@ -22,7 +22,7 @@ from tile_rule import _expected_tile
 pytestmark = pytest.mark.gpu
 
 MFMA_VARIANTS = ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_staged", "mfma_unpadded",
-                 "mfma_32", "mfma_dword", "mfma_32x64", "mfma_serial", "mfma_16"]
+                 "mfma_32", "mfma_dword", "mfma_32x64", "mfma_serial", "mfma_16", "mfma_64x96"]
 VALU_VARIANTS = ["naive", "lds", "reg", "dbuf"]
 ALL_VARIANTS = VALU_VARIANTS + MFMA_VARIANTS
 
@@ -239,7 +239,7 @@ EXTREME_SHAPES = [(1, 1, 1 << 22), (2, 3, 1 << 20), (1 << 20, 3, 7), (5, 1 << 20
 
 
 @pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged", "mfma_32",
-                                     "mfma_32x64", "mfma_serial", "mfma_16"])
+                                     "mfma_32x64", "mfma_serial", "mfma_16", "mfma_64x96"])
 @pytest.mark.parametrize("shape", EXTREME_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_extreme_aspect_ratios(variant, shape):
     M, N, K = shape
@@ -261,7 +261,7 @@ DMA_DIMS = [4, 8, 12, 28, 36, 60, 68, 124, 132, 252, 260, 516]
 
 @pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_unpadded",
                                      "mfma_32", "mfma_dword", "mfma_32x64", "mfma_serial",
-                                     "mfma_16"])
+                                     "mfma_16", "mfma_64x96"])
 def test_buffer_to_lds_edge_sweep(variant):
     g0 = np.random.default_rng(53 + MFMA_VARIANTS.index(variant))
     shapes = [tuple(int(x) for x in g0.choice(DMA_DIMS, 3)) for _ in range(20)]
@@ -306,7 +306,8 @@ def test_load_paths_agree_bitwise(w, tile):
 
 
 @pytest.mark.parametrize("variant", ["mfma", "mfma_256", "mfma_64", "mfma_staged", "lds", "reg",
-                                     "dbuf", "mfma_32", "mfma_dword", "mfma_32x64", "mfma_16"])
+                                     "dbuf", "mfma_32", "mfma_dword", "mfma_32x64", "mfma_16",
+                                     "mfma_64x96"])
 def test_padded_leading_dimensions(variant):
     """NaN in the padding of A and B must not reach C; C's padding is untouched."""
     M, N, K = 200, 136, 72
@@ -321,7 +322,7 @@ def test_padded_leading_dimensions(variant):
     assert np.all(np.isnan(C[:, N:])), "C padding columns were written"
 
 
-@pytest.mark.parametrize("variant", ["mfma", "mfma_128", "lds", "dbuf", "mfma_16"])
+@pytest.mark.parametrize("variant", ["mfma", "mfma_128", "lds", "dbuf", "mfma_16", "mfma_64x96"])
 def test_misaligned_pointers(variant):
     """Operands that start 4 bytes past a 16-byte boundary take the 32-bit path."""
     import torch
@@ -364,7 +365,9 @@ def test_expected_tile_on_256_cus():
     assert _expected_tile(512, 512, 512, 1, 256) == "mfma_32"
     assert _expected_tile(1000, 130, 1024, 1, 256) == "mfma_32"
     assert _expected_tile(1000, 130, 2048, 1, 256) == "mfma_32"
-    assert _expected_tile(1000, 1500, 777, 1, 256) == "mfma_32x64"
+    assert _expected_tile(1000, 1500, 777, 1, 256) == "mfma_64x96"    # 256 tiles, one round
+    assert _expected_tile(1000, 1700, 777, 1, 256) == "mfma_32"       # 288 tiles of 64 x 96
+    assert _expected_tile(1024, 1536, 1024, 1, 256) == "mfma_64x96"
     assert _expected_tile(1024, 1024, 1024, 1, 256) == "mfma_64"
     assert _expected_tile(2048, 2048, 2048, 1, 256) == "mfma_128"
     assert _expected_tile(8192, 8192, 8192, 1, 256) == "mfma_256"
@@ -455,7 +458,8 @@ def test_deterministic_bits_k_split_tile(M, N, K):
 # product.
 RACE_TRIAGE_SHAPES = [(256, 256, 256, 256), (512, 512, 512, 512), (768, 768, 768, 768),
                       (640, 640, 2048, 2048),
-                      (1000, 1500, 776, 776), (1000, 1500, 777, 777), (1024, 1024, 1024, 1024),
+                      (1000, 1500, 776, 776), (1000, 1500, 777, 777), (800, 1280, 777, 777),
+                      (1024, 1024, 1024, 1024),
                       (1024, 1024, 2048, 2048), (3072, 3072, 1024, 1024),
                       (2048, 2048, 2048, 2048), (4096, 4096, 1024, 1024), (300, 260, 100, 100),
                       (129, 67, 45, 45)]

@@ -43,7 +43,8 @@ WORKLOAD_CONFIGS = [
     ((256, 256, 1024, 1), (16, 16, 1024, 4)),
     ((512, 512, 512, 1), (32, 32, 64, 4)),        # 32 x 32, 64-float slices
     ((768, 768, 768, 1), (32, 32, 32, 4)),        # more work-groups than CUs: 32-float slices
-    ((1000, 1500, 777, 1), (32, 64, 32, 2)),
+    ((1000, 1500, 777, 1), (64, 96, 32, 2)),      # 256 tiles: one 12-wave work-group per CU
+    ((1000, 1700, 777, 1), (32, 32, 32, 4)),      # 288 tiles of 64 x 96: not one round
     ((640, 640, 2048, 1), (32, 64, 64, 2)),
     ((1024, 1024, 1024, 1), (64, 64, 32, 2)),     # two k sets of four waves
     ((1024, 1024, 2048, 1), (64, 64, 64, 2)),
