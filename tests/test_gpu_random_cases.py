@@ -1,12 +1,15 @@
 """Seeded random cases of the general form against the oracle.
 
-Each case draws a layout, sizes (1 .. 600, so every tile size and both sides
-of the 32 x 32 / 64 x 64 choice occur), alpha and beta (including 0 and 1),
-padded leading dimensions, a base pointer offset by 0 .. 3 floats (so
-16-byte and 4-byte loads both occur), and a batch of 1 .. 3 with gaps
-between the products; the result must meet the oracle's tolerance in every
-product, and padding and gaps must be left untouched.  The same cases run
-through the bfloat16 split entry point (one product each).
+Each case draws a layout, sizes, alpha and beta (including 0 and 1), padded
+leading dimensions, a base pointer offset by 0 .. 3 floats (so 16-byte and
+4-byte loads both occur), and a batch of 1 .. 3 with gaps between the
+products; the result must meet the oracle's tolerance in every product, and
+padding and gaps must be left untouched.  The small cases (sizes 1 .. 600)
+mostly run the 16 x 16 small-product kernel, with some 32 x 32 and 32 x 64
+tiles; the large cases run every buffer-to-LDS configuration but the 256 x
+256 one (which the 8192^3 tests of every layout cover), four times each.  The
+small cases also run through the bfloat16 split entry point (one product
+each).
 """
 import numpy as np
 import pytest
@@ -18,6 +21,7 @@ from dense_fp32_matrix_03_amd import inputs
 pytestmark = pytest.mark.gpu
 
 CASES = 400
+LARGE_CASES = 40
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -27,17 +31,35 @@ def library():
     sg.sgemm_destroy()
 
 
-def _case(seed):
+SMALL_DIMS = [1, 2, 3, 5, 16, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 200, 255, 256, 257,
+              300, 384, 511, 600]
+# (M, N, K, batch) of the large cases, one per buffer-to-LDS configuration
+# on 256 CUs, in turn; layout, alpha, beta, padding and offset are drawn.
+LARGE_SHAPES = [(1000, 1500, 777, 1),    # 64 x 96
+                (512, 768, 515, 4),      # 64 x 96, a batch filling one round
+                (2048, 2048, 256, 1),    # 128 x 128
+                (1024, 1024, 1024, 1),   # 64 x 64 in two k sets
+                (1024, 1024, 2048, 1),   # 64 x 64 in two k sets, 64-float slices
+                (2048, 1536, 100, 1),    # 64 x 64, four waves, three rounds
+                (800, 1280, 777, 1),     # 32 x 64
+                (640, 640, 1024, 1),     # 32 x 64 with 64-float slices
+                (768, 768, 777, 1),      # 32 x 32
+                (512, 500, 515, 1)]      # 32 x 32 with 64-float slices
+
+
+def _case(seed, large=False):
     g = np.random.default_rng(seed)
-    dims = [int(x) for x in g.choice([1, 2, 3, 5, 16, 31, 32, 33, 63, 64, 65, 100, 127, 128,
-                                      129, 200, 255, 256, 257, 300, 384, 511, 600], 3)]
-    M, N, K = dims
+    if large:
+        M, N, K, batch = LARGE_SHAPES[seed % len(LARGE_SHAPES)]
+    else:
+        M, N, K = (int(x) for x in g.choice(SMALL_DIMS, 3))
     ta, tb = bool(g.integers(0, 2)), bool(g.integers(0, 2))
     alpha = float(g.choice([1.0, -1.0, 0.5, 2.0, 0.0]))
     beta = float(g.choice([0.0, 1.0, -0.75, 0.0]))
     pad_a, pad_b, pad_c = (int(x) for x in g.integers(0, 5, 3))
     offset = int(g.integers(0, 4))
-    batch = int(g.integers(1, 4))
+    if not large:
+        batch = int(g.integers(1, 4))
     return g, M, N, K, ta, tb, alpha, beta, pad_a, pad_b, pad_c, offset, batch
 
 
@@ -49,8 +71,17 @@ def _layout(ta, tb, M, N, K, pad_a, pad_b):
 
 @pytest.mark.parametrize("seed", range(CASES))
 def test_general_form_random_case(seed):
+    _general_case(10_000 + seed, False)
+
+
+@pytest.mark.parametrize("seed", range(LARGE_CASES))
+def test_general_form_random_large_case(seed):
+    _general_case(30_000 + seed, True)
+
+
+def _general_case(seed, large):
     import torch
-    g, M, N, K, ta, tb, alpha, beta, pad_a, pad_b, pad_c, offset, batch = _case(10_000 + seed)
+    g, M, N, K, ta, tb, alpha, beta, pad_a, pad_b, pad_c, offset, batch = _case(seed, large)
     ar, ac, lda, br, bc, ldb = _layout(ta, tb, M, N, K, pad_a, pad_b)
     ldc = N + pad_c
     sA, sB, sC = ar * lda + 7, br * ldb + 5, M * ldc + 3
