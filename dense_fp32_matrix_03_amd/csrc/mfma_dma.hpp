@@ -253,9 +253,9 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
     else return Bs3;
   };
   // Partial sums that each k set hands to the others for the final
-  // reduction (one slot per set; a set's own registers stay unwritten).
+  // reduction (per set, the registers of the other sets).
   constexpr int kRedSlot = NWT * FM * FN * 16 * kWave;
-  __shared__ __attribute__((aligned(1024))) float Red[KSPLIT > 1 ? KSPLIT * kRedSlot : 1];
+  __shared__ __attribute__((aligned(1024))) float Red[KSPLIT > 1 ? (KSPLIT - 1) * kRedSlot : 1];
   // Landing area of the spare loads (zeros, never read).
   __shared__ __attribute__((aligned(1024))) float Dump[GA::SPARE || GB::SPARE ? 4 * kWave : 1];
 
@@ -496,45 +496,64 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   // everything belongs to set 0.
   static_assert(16 % KSPLIT == 0, "k sets must share the 16 registers of a block evenly");
   constexpr int EPS = 16 / KSPLIT;
-  auto slot = [&](int q, int i, int j, int e) {
-    return ((((q * NWT + wl) * FM + i) * FN + j) * 16 + e) * kWave + lane;
+  // Register r EPS + ee of block (i, j) for a set number r that is the same
+  // in the whole wave but not a compile-time constant: picked by selects
+  // (indexed by r, the registers were moved with indexed register moves).
+  auto reg = [&](int i, int j, int r, int ee) {
+    float v = acc[i][j][ee];
+#pragma unroll
+    for (int s = 1; s < KSPLIT; ++s) v = r == s ? acc[i][j][s * EPS + ee] : v;
+    return v;
   };
+  // Slot of writer set w in LDS for the registers of the p-th set other than
+  // w (sets in increasing order), block (i, j), register ee of that set's range.
+  auto slot = [&](int w, int pos, int i, int j, int ee) {
+    return (((((w * (KSPLIT - 1) + pos) * NWT + wl) * FM + i) * FN + j) * EPS + ee) * kWave + lane;
+  };
+  float res[FM][FN][EPS];  // the reduced sums of set kq's registers
   if constexpr (KSPLIT > 1) {
     // Every set leaves in LDS the registers the other sets own; after the
-    // barrier each set adds, for its own registers, the sums of sets 0, 1,
-    // .., KSPLIT-1 in that order.  The additions and the stores of C are
-    // shared by all sets, and each element is the same sum, in the same
+    // barrier each set adds, for its own registers, the partial sums of sets
+    // 0, 1, .., KSPLIT-1 in that order.  The additions and the stores of C
+    // are shared by all sets, and each element is the same sum, in the same
     // order, as when one set adds up all of them.
-    static_for<KSPLIT>([&](auto Q) {
-      constexpr int q = decltype(Q)::value;
-      if (kq == q) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+    for (int pos = 0; pos < KSPLIT - 1; ++pos) {
+      const int r = pos + (pos >= kq ? 1 : 0);
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-              if (e / EPS != q) Red[slot(q, i, j, e)] = acc[i][j][e];
-      }
-    });
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int ee = 0; ee < EPS; ++ee) Red[slot(kq, pos, i, j, ee)] = reg(i, j, r, ee);
+    }
     __syncthreads();
-    static_for<KSPLIT>([&](auto Q) {
-      constexpr int q = decltype(Q)::value;
-      if (kq == q) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int ee = 0; ee < EPS; ++ee) {
-              const int e = q * EPS + ee;
-              float sum = q == 0 ? acc[i][j][e] : Red[slot(0, i, j, e)];
+        for (int ee = 0; ee < EPS; ++ee) {
+          const float mine = reg(i, j, kq, ee);
+          if constexpr (KSPLIT == 2) {
+            // the two-term sum in either order: IEEE addition is commutative
+            res[i][j][ee] = mine + Red[slot(1 - kq, 0, i, j, ee)];
+          } else {
+            // o[pos]: the partial sums of the pos-th other set w, which left
+            // set kq's registers at its position kq - (kq > w)
+            float o[KSPLIT - 1];
 #pragma unroll
-              for (int r = 1; r < KSPLIT; ++r) sum += r == q ? acc[i][j][e] : Red[slot(r, i, j, e)];
-              acc[i][j][e] = sum;
+            for (int pos = 0; pos < KSPLIT - 1; ++pos) {
+              const int w = pos + (pos >= kq ? 1 : 0);
+              o[pos] = Red[slot(w, kq - (kq > w ? 1 : 0), i, j, ee)];
             }
-      }
-    });
+            float sum = kq == 0 ? mine : o[0];
+#pragma unroll
+            for (int r = 1; r < KSPLIT; ++r)
+              sum += r < kq ? o[r < KSPLIT - 1 ? r : KSPLIT - 2] : (r == kq ? mine : o[r - 1]);
+            res[i][j][ee] = sum;
+          }
+        }
   }
 
   phase(3);
@@ -546,7 +565,8 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   // that do not follow a read of C are non-temporal: C is not read again by
   // this kernel, and streaming it out instead of leaving it dirty in L2 took
   // 2048^3 from 144.3 to 146.1 TFLOP/s (1024^3: 112.6 to 114.1).  Each k set
-  // stores the registers it owns.
+  // stores the registers it owns (with k sets, the stores after a read of C
+  // are non-temporal as well).
   const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN + r32;
   const bool full = (m0 + BM <= p.M) && (n0 + BN <= p.N);
   const bool plain = p.alpha == 1.f && p.beta == 0.f;
@@ -580,37 +600,43 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
         }
       }
   } else {
-    // Set q stores registers q EPS .. q EPS + EPS - 1 of each block.
-    static_for<KSPLIT>([&](auto Q) {
-      constexpr int e0 = decltype(Q)::value * EPS;
-      if (kq == decltype(Q)::value) {
+    // Set kq stores its registers kq EPS + ee of each block: rows
+    // 2 kq EPS + 8 (ee / 4) + ee % 4 of the block (+ 4 for the upper half of
+    // the lanes).  Full tiles store without tests.
+    const int rq = row0 + 2 * kq * EPS + 4 * half;
+    auto dr = [](int ee) { return 8 * (ee >> 2) + (ee & 3); };
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int col = col0 + j * 32;
-            auto row = [&](int e) { return row0 + i * 32 + acc32_row(lane, e); };
-            auto inside = [&](int e) { return full || (row(e) < p.M && col < p.N); };
-            auto at = [&](int e) { return Cb + (long)row(e) * p.ldc + col; };
-            if (plain) {
+      for (int j = 0; j < FN; ++j) {
+        const int col = col0 + j * 32;
+        const int rb = rq + i * 32;
+        float *const at0 = Cb + (long)rb * p.ldc + col;
+        auto at = [&](int ee) { return at0 + (long)dr(ee) * p.ldc; };
+        auto inside = [&](int ee) { return rb + dr(ee) < p.M && col < p.N; };
+        if (plain || p.beta == 0.f) {
+          float v[EPS];
 #pragma unroll
-              for (int e = e0; e < e0 + EPS; ++e)
-                if (inside(e)) __builtin_nontemporal_store(acc[i][j][e], at(e));
-            } else if (p.beta == 0.f) {
+          for (int ee = 0; ee < EPS; ++ee) v[ee] = plain ? res[i][j][ee] : p.alpha * res[i][j][ee];
+          if (full) {
 #pragma unroll
-              for (int e = e0; e < e0 + EPS; ++e)
-                if (inside(e)) __builtin_nontemporal_store(p.alpha * acc[i][j][e], at(e));
-            } else {
-              float c[EPS];
+            for (int ee = 0; ee < EPS; ++ee) __builtin_nontemporal_store(v[ee], at(ee));
+          } else {
 #pragma unroll
-              for (int e = e0; e < e0 + EPS; ++e) c[e - e0] = inside(e) ? *at(e) : 0.f;
-#pragma unroll
-              for (int e = e0; e < e0 + EPS; ++e)
-                if (inside(e)) *at(e) = fmaf(p.alpha, acc[i][j][e], p.beta * c[e - e0]);
-            }
+            for (int ee = 0; ee < EPS; ++ee)
+              if (inside(ee)) __builtin_nontemporal_store(v[ee], at(ee));
           }
+        } else {
+          float c[EPS];
+#pragma unroll
+          for (int ee = 0; ee < EPS; ++ee) c[ee] = full || inside(ee) ? *at(ee) : 0.f;
+#pragma unroll
+          for (int ee = 0; ee < EPS; ++ee)  // non-temporal as well: the compiler merges the
+            if (full || inside(ee))          // last store of each path into one store, which
+              __builtin_nontemporal_store(   // keeps the hint only if all of them carry it
+                  fmaf(p.alpha, res[i][j][ee], p.beta * c[ee]), at(ee));
+        }
       }
-    });
   }
   if constexpr (PHASES) {
     __builtin_amdgcn_s_waitcnt(0);
