@@ -268,7 +268,7 @@ __device__ __forceinline__ int bf16_swizzle(int row) {
 //      0 while the three of order 2 run (four plane sets live).
 template <int BM, int BN, int BK, int WM, int WN, int MODE, int NS>
 __global__ void __launch_bounds__(WM *WN *kWave)
-bf16x3_gemm_kernel(Bf16x3Args p, int tiles_m, int tiles_n, int group_m) {
+bf16x3_gemm_kernel(Bf16x3Args p, TileMap tmap) {
   static_assert(NS >= 2 && NS <= 4, "two to four stages");
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -313,9 +313,8 @@ bf16x3_gemm_kernel(Bf16x3Args p, int tiles_m, int tiles_n, int group_m) {
   const int wm = wave / WN, wn = wave % WN;
   const int r32 = lane % 32, half = lane / 32;
 
-  const int id = xcd_contiguous_id(blockIdx.x, gridDim.x);
-  int tm, tn;
-  grouped_tile(id, tiles_m, tiles_n, group_m, tm, tn);
+  int bidx, tm, tn;  // one product: bidx is 0
+  tmap.tile(xcd_contiguous_id(blockIdx.x, gridDim.x), bidx, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const long Kp = p.Kp;
 
@@ -526,7 +525,7 @@ static hipError_t launch_bf16x3_cfg(const Bf16x3Args &p, hipStream_t stream) {
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   hipLaunchKernelGGL((bf16x3_gemm_kernel<BM, BN, BK, WM, WN, MODE, NS>),
                      dim3((unsigned)((long)tiles_m * tiles_n)), dim3(WM * WN * kWave), 0, stream,
-                     p, tiles_m, tiles_n, 8);
+                     p, make_tile_map(tiles_m, tiles_n, 8));
   return hipGetLastError();
 }
 

@@ -37,24 +37,67 @@ __device__ __forceinline__ int acc32_row(int lane, int j) {
 // below gives each XCD a compact patch of C whose A rows and B columns it
 // re-reads from its own L2.
 __device__ __forceinline__ int xcd_contiguous_id(int w, int nwg) {
-  constexpr int kXcds = 8;
-  const int q = nwg / kXcds, r = nwg % kXcds;
-  const int x = w % kXcds, local = w / kXcds;
-  return x * q + (x < r ? x : r) + local;
+  constexpr unsigned kXcds = 8;
+  const unsigned q = (unsigned)nwg / kXcds, r = (unsigned)nwg % kXcds;
+  const unsigned x = (unsigned)w % kXcds, local = (unsigned)w / kXcds;
+  return (int)(x * q + (x < r ? x : r) + local);
 }
 
-// Launch position -> (tile row, tile column) with a grouped raster: groups of
-// `group_m` tile rows, walked column by column inside a group, so work-groups
-// that run together share both A row panels and B column panels.
-__device__ __forceinline__ void grouped_tile(int id, int tiles_m, int tiles_n, int group_m,
-                                             int &tm, int &tn) {
-  const int per_group = group_m * tiles_n;
-  const int g = id / per_group;
-  const int first = g * group_m;
-  const int rows = min(tiles_m - first, group_m);
-  const int in = id - g * per_group;
-  tm = first + in % rows;
-  tn = in / rows;
+// Division by a divisor that is fixed for a launch, as one multiply and one
+// shift (T. Granlund and P. L. Montgomery, "Division by invariant integers
+// using multiplication", PLDI 1994, Theorem 4.2 with N = 31): for
+// 1 <= d < 2^31, with l = ceil(log2 d) and m = ceil(2^(31+l) / d), which
+// fits in 32 bits, floor(n / d) = floor(n m / 2^(31+l)) for every
+// 0 <= n < 2^31.  The work-group -> tile maps divide by such divisors, built
+// on the host, so a work-group spends a few scalar instructions before its
+// first load instead of a reciprocal sequence per division.
+struct FastDiv {
+  unsigned m;
+  int shift;
+  __host__ __device__ __forceinline__ int operator()(int n) const {
+    return (int)(((unsigned long long)(unsigned)n * m) >> shift);
+  }
+};
+
+inline FastDiv make_fast_div(int d) {  // host side; 1 <= d < 2^31
+  int l = 0;
+  while ((1LL << l) < d) ++l;
+  const unsigned long long p = 1ULL << (31 + l), dd = (unsigned long long)d;
+  return FastDiv{(unsigned)((p + dd - 1) / dd), 31 + l};
+}
+
+// Launch position -> (product of the batch, tile row, tile column).  Tiles
+// follow a grouped raster: groups of `group_m` tile rows, walked column by
+// column inside a group, so work-groups that run together share both A row
+// panels and B column panels.  Built once per launch (make_tile_map).
+struct TileMap {
+  int tiles_m, tiles_n, group_m;
+  FastDiv by_tiles;        // tiles_m tiles_n: which product of the batch
+  FastDiv by_group_tiles;  // group_m tiles_n: which group of tile rows
+  FastDiv by_group_m;      // the rows of a full group
+  FastDiv by_last_rows;    // the rows of a last, partial group
+  __host__ __device__ __forceinline__ void tile(int id, int &bidx, int &tm, int &tn) const {
+    bidx = by_tiles(id);
+    const int t = id - bidx * (tiles_m * tiles_n);
+    const int g = by_group_tiles(t);
+    const int first = g * group_m;
+    const int in = t - g * (group_m * tiles_n);
+    const bool partial = first + group_m > tiles_m;
+    const int rows = partial ? tiles_m - first : group_m;
+    tn = partial ? by_last_rows(in) : by_group_m(in);
+    tm = first + (in - tn * rows);
+  }
+};
+
+inline TileMap make_tile_map(int tiles_m, int tiles_n, int group_m) {  // host side
+  const int last = tiles_m % group_m;
+  return TileMap{tiles_m,
+                 tiles_n,
+                 group_m,
+                 make_fast_div(tiles_m * tiles_n),
+                 make_fast_div(group_m * tiles_n),
+                 make_fast_div(group_m),
+                 make_fast_div(last ? last : group_m)};
 }
 
 }  // namespace sgemm

@@ -195,7 +195,7 @@ struct SliceGeom {
 template <int BM, int BN, int BK, int WM, int WN, bool SWZ, bool KFULL, int SCHED, bool VA,
           bool VB, bool TA, bool TB, int KSPLIT = 1, int NST = 2, bool PHASES = false>
 __global__ void __launch_bounds__(WM *WN *KSPLIT *kWave)
-mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
+mfma_gemm_dma_kernel(GemmArgs p, TileMap tmap) {
   auto phase = [&](int i) {
     if constexpr (PHASES) {
       if (threadIdx.x == 0) p.phases[(long)blockIdx.x * 8 + i] = __builtin_amdgcn_s_memrealtime();
@@ -269,11 +269,8 @@ mfma_gemm_dma_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   const int r32 = lane % 32, half = lane / 32;
 
   // Launch position -> (product of the batch, tile).
-  const int tiles = tiles_m * tiles_n;
-  const int id = xcd_contiguous_id(blockIdx.x, gridDim.x);
-  const int bidx = id / tiles;
-  int tm, tn;
-  grouped_tile(id - bidx * tiles, tiles_m, tiles_n, group_m, tm, tn);
+  int bidx, tm, tn;
+  tmap.tile(xcd_contiguous_id(blockIdx.x, gridDim.x), bidx, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const float *Ab = p.A + (long)bidx * p.strideA;
   const float *Bb = p.B + (long)bidx * p.strideB;
@@ -651,14 +648,15 @@ inline void launch_dma_kernel(const GemmArgs &p, hipStream_t stream, int group_m
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const dim3 grid((unsigned)((long)tiles_m * tiles_n * p.batch)),
       block(WM * WN * KSPLIT * kWave);
+  const TileMap tmap = make_tile_map(tiles_m, tiles_n, group_m);
   if (p.K % BK == 0)
     hipLaunchKernelGGL((mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, true, SCHED, VA, VB, TA, TB,
                                              KSPLIT, NST, PHASES>),
-                       grid, block, 0, stream, p, tiles_m, tiles_n, group_m);
+                       grid, block, 0, stream, p, tmap);
   else
     hipLaunchKernelGGL((mfma_gemm_dma_kernel<BM, BN, BK, WM, WN, SWZ, false, SCHED, VA, VB, TA,
                                              TB, KSPLIT, NST, PHASES>),
-                       grid, block, 0, stream, p, tiles_m, tiles_n, group_m);
+                       grid, block, 0, stream, p, tmap);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool SWZ, int SCHED, bool TA, bool TB,

@@ -52,7 +52,7 @@ namespace sgemm {
 
 template <int BM, int BN, int BK, int WM, int WN, int APAD, int STORE_G, bool VA, bool VB>
 __global__ void __launch_bounds__(WM *WN *kWave)
-mfma_gemm_staged_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
+mfma_gemm_staged_kernel(GemmArgs p, TileMap tmap) {
   constexpr int NT = WM * WN * kWave;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -78,8 +78,8 @@ mfma_gemm_staged_kernel(GemmArgs p, int tiles_m, int tiles_n, int group_m) {
   const int wm = wave / WN, wn = wave % WN;
   const int r32 = lane % 32, half = lane / 32;
 
-  int tm, tn;
-  grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
+  int bidx, tm, tn;  // one product: bidx is 0
+  tmap.tile(xcd_contiguous_id(blockIdx.x, gridDim.x), bidx, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   FetchA fa;
@@ -181,10 +181,11 @@ inline hipError_t launch_staged_cfg(const GemmArgs &p, bool va, bool vb, hipStre
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const long nwg = (long)tiles_m * tiles_n;
   const dim3 grid((unsigned)nwg), block(WM * WN * kWave);
+  const TileMap tmap = make_tile_map(tiles_m, tiles_n, group_m);
 #define SGEMM_STAGED_LAUNCH(VA_, VB_)                                                             \
   hipLaunchKernelGGL(                                                                           \
       (mfma_gemm_staged_kernel<BM, BN, BK, WM, WN, APAD, STORE_G, VA_, VB_>), grid, block, \
-      0, stream, p, tiles_m, tiles_n, group_m)
+      0, stream, p, tmap)
   if (va && vb)
     SGEMM_STAGED_LAUNCH(true, true);
   else if (va)

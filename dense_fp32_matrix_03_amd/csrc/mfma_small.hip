@@ -40,7 +40,7 @@ constexpr int kSmallWaves = 4;
 // are four 4-byte loads.
 template <int NG, bool TA, bool TB, bool WA, bool WB, bool PHASES>
 __global__ void __launch_bounds__(kSmallWaves *kWave)
-mfma_small_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+mfma_small_kernel(GemmArgs p, TileMap tmap) {
   auto phase = [&](int i) {
     if constexpr (PHASES) {
       if (threadIdx.x == 0) p.phases[(long)blockIdx.x * 8 + i] = __builtin_amdgcn_s_memrealtime();
@@ -62,11 +62,8 @@ mfma_small_kernel(GemmArgs p, int tiles_m, int tiles_n) {
 
   // Launch position -> (product of the batch, tile), tiles row by row inside
   // the share of consecutive ids that one XCD receives.
-  const int tiles = tiles_m * tiles_n;
-  const int id = xcd_contiguous_id(blockIdx.x, gridDim.x);
-  const int bidx = id / tiles;
-  const int t = id - bidx * tiles;
-  const int tm = t / tiles_n, tn = t - tm * tiles_n;
+  int bidx, tm, tn;
+  tmap.tile(xcd_contiguous_id(blockIdx.x, gridDim.x), bidx, tm, tn);
   const float *Ab = p.A + (long)bidx * p.strideA;
   const float *Bb = p.B + (long)bidx * p.strideB;
   float *Cb = p.C + (long)bidx * p.strideC;
@@ -162,9 +159,10 @@ void launch_ng(const GemmArgs &p, bool wa, bool wb, hipStream_t stream) {
   const int tiles_m = (p.M + kSmallTile - 1) / kSmallTile;
   const int tiles_n = (p.N + kSmallTile - 1) / kSmallTile;
   const dim3 grid((unsigned)((long)tiles_m * tiles_n * p.batch)), block(kSmallWaves * kWave);
+  const TileMap tmap = make_tile_map(tiles_m, tiles_n, 1);  // groups of one row: row by row
 #define SGEMM_SMALL_LAUNCH(WA_, WB_)                                                        \
   hipLaunchKernelGGL((mfma_small_kernel<NG, TA, TB, WA_, WB_, PHASES>), grid, block, 0, stream, \
-                     p, tiles_m, tiles_n)
+                     p, tmap)
   if constexpr (!TA && TB) {
     if (wa && wb) SGEMM_SMALL_LAUNCH(true, true);
     else if (wa) SGEMM_SMALL_LAUNCH(true, false);
