@@ -105,16 +105,18 @@ TileChoice with_slice_rule(MfmaTile tile, long M, long N, long K, int cus, long 
 // 512^3 and 1000 x 130 x 2048 take 32 x 32; 256^3 16 x 16.
 //
 // The 16 x 16 small-product tile, measured on 256 CUs against the best
-// buffer-to-LDS tile (kernel trace): 256^3 4.88 -> 3.79 us, 256 x 256 x 1024
-// 8.07 -> 6.71, 128^3 4.29 -> 3.09, 512 x 512 x 64 4.25 -> 3.93, 100 x 3000
-// x 64 4.83 -> 4.55 (its tiles read 4-50 KiB per CU, or 128 KiB where the
-// 32 x 32 tile fills a quarter of the CUs).  Where its tiles read 64-100 KiB
-// per CU and a buffer-to-LDS tile keeps at least half the matrix-core time
-// on C it loses (384 x 384 x 256: 5.29 against 5.01; 768 x 256 x 256: 5.26
-// against 5.02; 512 x 512 x 128: 4.79 against 4.66; 640 x 640 x 128: 5.73
-// against 5.22), and past 128 KiB per CU it loses by more (384 x 384 x 512:
-// 7.50 against 6.07; 1000 x 130 x 1024: 16.50 against 9.41).  Shapes with
-// more than 8 of its tiles per CU were not measured.
+// buffer-to-LDS tile (kernel trace): 256^3 4.33 -> 3.74 us, 256 x 256 x 1024
+// 7.46 -> 6.61, 128^3 3.88 -> 3.09, 256^2 x 32 3.70 -> 2.92 (its tiles read
+// 4-32 KiB per CU, or 128 KiB where the 32 x 32 tile fills a quarter of the
+// CUs), even on 512 x 512 x 64 (32 KiB) and 100 x 3000 x 64 (41 KiB).  At 50
+// KiB per CU it loses (640 x 640 x 64: 4.38-4.81 against 4.11-4.60 over
+// three sweeps), and where its tiles read 64-100 KiB per CU and a
+// buffer-to-LDS tile keeps at least half the matrix-core time on C it loses
+// more (384 x 384 x 256: 5.48 against 4.65; 768 x 256 x 256: 5.28 against
+// 4.52; 512 x 512 x 128: 4.31 against 4.03; 640 x 640 x 128: 5.52 against
+// 4.64), and past 128 KiB per CU by more still (384 x 384 x 512: 7.81
+// against 5.71; 1000 x 130 x 1024: 16.06 against 8.79).  Shapes with more
+// than 8 of its tiles per CU were not measured.
 TileChoice choose_mfma_tile(long M, long N, long K, int cus, long batch) {
   auto eff = [&](const TileShape &t) {
     if (t.tile == MfmaTile::T16) return 0.0;
@@ -126,7 +128,7 @@ TileChoice choose_mfma_tile(long M, long N, long K, int cus, long batch) {
   double best = 0.0;
   for (const TileShape &t : kTileShapes) best = fmax(best, eff(t));
   if (small_product(M, N, K, cus, batch) &&
-      (small_bytes_per_cu(M, N, K, cus, batch) <= 56.0 * 1024 || best < 0.5))
+      (small_bytes_per_cu(M, N, K, cus, batch) <= 48.0 * 1024 || best < 0.5))
     return with_slice_rule(MfmaTile::T16, M, N, K, cus, batch);
   for (const TileShape &t : kTileShapes)
     if (best > 0.0 && eff(t) >= 0.97 * best) return with_slice_rule(t.tile, M, N, K, cus, batch);

@@ -89,7 +89,7 @@ extern "C" {
  * the compute units.  A product with K <= 1024, at most 8 tiles of 16 x 16 per
  * compute unit and at most 128 KiB of operand reads per compute unit on
  * those tiles (128 K bytes per tile) takes the 16 x 16 tile instead when
- * those reads stay within 56 KiB per compute unit or the best of the other
+ * those reads stay within 48 KiB per compute unit or the best of the other
  * tiles would spend under half of the matrix-core time on C.  The
  * _MFMA_<n> variants force a tile (with the same rule for its form): the
  * 64 x 64 tile runs four waves, or two sets of four when its work-groups fit

@@ -358,6 +358,7 @@ def test_expected_tile_on_256_cus():
     assert _expected_tile(512, 512, 64, 1, 256) == "mfma_16"
     assert _expected_tile(512, 512, 128, 1, 256) == "mfma_32"    # 64 KiB per CU
     assert _expected_tile(100, 3000, 64, 1, 256) == "mfma_16"    # 41 KiB per CU
+    assert _expected_tile(640, 640, 64, 1, 256) == "mfma_32x64"  # 50 KiB per CU
     assert _expected_tile(512, 512, 256, 1, 256) == "mfma_32"    # 128 KiB, 32 x 32 fills the CUs
     assert _expected_tile(256, 256, 1024, 1, 256) == "mfma_16"   # at the traffic bound
     assert _expected_tile(384, 384, 512, 1, 256) == "mfma_32"    # over it

@@ -28,7 +28,7 @@ def _expected_tile(M, N, K, batch, cus):
         return float(M) * N * batch / (rounds * cus * bm * bn)
     best = max(eff(*t) for t in TILE_RULE)
     tiles16 = -(-M // 16) * -(-N // 16) * batch
-    if _small_product(M, N, K, batch, cus) and (tiles16 * K * 128 <= 56 * 1024 * cus
+    if _small_product(M, N, K, batch, cus) and (tiles16 * K * 128 <= 48 * 1024 * cus
                                                  or best < 0.5):
         return "mfma_16"
     for t in TILE_RULE:
