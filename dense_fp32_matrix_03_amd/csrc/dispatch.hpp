@@ -22,8 +22,14 @@ enum class MfmaTile { T256, T128, T64x96, T64, T32x64, T32, T16 };
 //    halve its cost.
 //  - The 64 x 64 tile takes two k sets (8 waves) when its work-groups fit
 //    one round and K >= 512 (1024^3: 18.95 -> 18.4 us), with 64-float slices
-//    from K >= 2048, where each k set's half of a 32-float slice is too
-//    little work between barriers (1024 x 1024 x 2048: 34.3 -> 33.2 us).
+//    from K >= 1280.  Each XCD's 32 work-groups read 8 tile rows of A and 4
+//    tile columns of B, 3 KiB per k; up to K = 1280 that fits the XCD's 4 MB
+//    L2 and back-to-back calls find their operands there, beyond it the
+//    operands come from farther away, and a 32-float slice (0.43 us of
+//    matrix work per SIMD at 1024^2) does not cover that latency: 1024 x
+//    1024 x 1408 takes 28.8 us on 32-float slices against 24.0 on 64-float
+//    ones, 1024^2 x 1536 31.5 against 26.1, while 1024^2 x 1152 and 1280 take
+//    the same time on both and 1024^3 is 1.5 % faster on 32-float slices.
 //    Otherwise the four-wave form: with several work-groups per CU, or few
 //    K slices, the eight-wave form loses (1024 products of 64^3: 9.8 against
 //    16.2 us; 3072 x 3072 x 1024: 136.8 against 139.6 us).

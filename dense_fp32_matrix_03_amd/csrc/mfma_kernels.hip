@@ -89,7 +89,7 @@ TileChoice with_slice_rule(MfmaTile tile, long M, long N, long K, int cus, long 
     const bool one_round = tile_count(M, N, t.bm, t.bn, batch) <= cus;
     if (form == MfmaTile::T64) {
       c.ksplit = one_round && K >= 512;
-      c.long_k = c.ksplit && K >= 2048;
+      c.long_k = c.ksplit && K >= 1280;
     } else if (form == MfmaTile::T32x64 || form == MfmaTile::T32) {
       c.long_k = one_round;
     }

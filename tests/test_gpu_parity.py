@@ -456,12 +456,14 @@ def test_deterministic_bits_k_split_tile(M, N, K):
 # unchanged); 32 x 32 with 64- and 32-float K slices, 32 x 64 with both,
 # 64 x 64 in two k sets with both, 64 x 64 in four waves, 128 x 128,
 # 256 x 256; and a ragged K, an unaligned A (lda = 777) and an odd-sized
-# product.
+# product; and 64-float slices on the 64 x 64 tile in two k sets with a
+# ragged K (1300) and with 4-byte A loads (lda = 1283).
 RACE_TRIAGE_SHAPES = [(256, 256, 256, 256), (512, 512, 512, 512), (768, 768, 768, 768),
                       (640, 640, 2048, 2048),
                       (1000, 1500, 776, 776), (1000, 1500, 777, 777), (800, 1280, 777, 777),
                       (1024, 1024, 1024, 1024),
-                      (1024, 1024, 2048, 2048), (3072, 3072, 1024, 1024),
+                      (1024, 1024, 2048, 2048), (896, 896, 1300, 1300), (832, 960, 1283, 1283),
+                      (3072, 3072, 1024, 1024),
                       (2048, 2048, 2048, 2048), (4096, 4096, 1024, 1024), (300, 260, 100, 100),
                       (129, 67, 45, 45)]
 

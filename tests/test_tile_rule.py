@@ -47,6 +47,9 @@ WORKLOAD_CONFIGS = [
     ((1000, 1700, 777, 1), (32, 32, 32, 4)),      # 288 tiles of 64 x 96: not one round
     ((640, 640, 2048, 1), (32, 64, 64, 2)),
     ((1024, 1024, 1024, 1), (64, 64, 32, 2)),     # two k sets of four waves
+    ((1024, 1024, 1152, 1), (64, 64, 32, 2)),
+    ((1024, 1024, 1280, 1), (64, 64, 64, 2)),     # 64-float slices from K = 1280
+    ((1024, 1024, 1536, 1), (64, 64, 64, 2)),
     ((1024, 1024, 2048, 1), (64, 64, 64, 2)),
     ((3072, 3072, 1024, 1), (64, 64, 32, 1)),     # several work-groups per CU: four waves
     ((2048, 2048, 2048, 1), (128, 128, 32, 1)),
