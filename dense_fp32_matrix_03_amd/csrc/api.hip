@@ -92,6 +92,26 @@ int check_args(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, con
 }
 
 inline bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+inline bool aligned4(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 3u) == 0; }
+
+// Which operands take 16-byte loads (sgemm::LoadWidths).  The small-product
+// and register-staged kernels load 16-byte aligned chunks: the base, the
+// leading dimension, the batch stride and the stored width must allow that.
+// The buffer-to-LDS kernel loads 16-byte chunks from any dword-aligned
+// address (its partial last K slice takes 4-byte loads where a chunk would
+// reach past K), so it needs a stored width that is a multiple of 4 only
+// where the chunks run along m or n: A stored transposed, B as given.
+sgemm::LoadWidths load_widths(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const float *A,
+                              int64_t lda, int64_t strideA, const float *B, int64_t ldb,
+                              int64_t strideB) {
+  const int64_t a_cols = ta ? M : K, b_cols = tb ? K : N;
+  sgemm::LoadWidths w;
+  w.a16 = aligned16(A) && lda % 4 == 0 && strideA % 4 == 0 && a_cols % 4 == 0;
+  w.b16 = aligned16(B) && ldb % 4 == 0 && strideB % 4 == 0 && b_cols % 4 == 0;
+  w.a_dma = aligned4(A) && (!ta || M % 4 == 0);
+  w.b_dma = aligned4(B) && (tb || N % 4 == 0);
+  return w;
+}
 
 }  // namespace
 
@@ -156,8 +176,7 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
   if (K == 0) {
     err = sgemm::launch_scale(p, s);  // beta = 0: zeros
   } else {
-    const bool va = aligned16(A) && lda % 4 == 0 && K % 4 == 0;
-    const bool vb = aligned16(B) && ldb % 4 == 0 && N % 4 == 0;
+    const sgemm::LoadWidths w = load_widths(false, false, M, N, K, A, lda, 0, B, ldb, 0);
     using sgemm::MfmaPath;
     using sgemm::MfmaTile;
     const sgemm::TileChoice autotile = sgemm::choose_mfma_tile(M, N, K, di.cus);
@@ -169,45 +188,45 @@ int sgemm_run_variant(int variant, int64_t M, int64_t N, int64_t K, const float 
       case SGEMM_VARIANT_LDS:
       case SGEMM_VARIANT_REG:
       case SGEMM_VARIANT_DBUF:
-        err = sgemm::launch_valu(variant - SGEMM_VARIANT_NAIVE, p, va, vb, s);
+        err = sgemm::launch_valu(variant - SGEMM_VARIANT_NAIVE, p, w.a16, w.b16, s);
         break;
       case SGEMM_VARIANT_MFMA_256:
-        err = sgemm::launch_mfma(forced(MfmaTile::T256), MfmaPath::Auto, p, va, vb, s);
+        err = sgemm::launch_mfma(forced(MfmaTile::T256), MfmaPath::Auto, p, w, s);
         break;
       case SGEMM_VARIANT_MFMA_128:
-        err = sgemm::launch_mfma(forced(MfmaTile::T128), MfmaPath::Auto, p, va, vb, s);
+        err = sgemm::launch_mfma(forced(MfmaTile::T128), MfmaPath::Auto, p, w, s);
         break;
       case SGEMM_VARIANT_MFMA_64:
-        err = sgemm::launch_mfma(forced(MfmaTile::T64), MfmaPath::Auto, p, va, vb, s);
+        err = sgemm::launch_mfma(forced(MfmaTile::T64), MfmaPath::Auto, p, w, s);
         break;
       case SGEMM_VARIANT_MFMA_64X96:
-        err = sgemm::launch_mfma(forced(MfmaTile::T64x96), MfmaPath::Auto, p, va, vb, s);
+        err = sgemm::launch_mfma(forced(MfmaTile::T64x96), MfmaPath::Auto, p, w, s);
         break;
       case SGEMM_VARIANT_MFMA_32X64:
-        err = sgemm::launch_mfma(forced(MfmaTile::T32x64), MfmaPath::Auto, p, va, vb, s);
+        err = sgemm::launch_mfma(forced(MfmaTile::T32x64), MfmaPath::Auto, p, w, s);
         break;
       case SGEMM_VARIANT_MFMA_32:
-        err = sgemm::launch_mfma(forced(MfmaTile::T32), MfmaPath::Auto, p, va, vb, s);
+        err = sgemm::launch_mfma(forced(MfmaTile::T32), MfmaPath::Auto, p, w, s);
         break;
       case SGEMM_VARIANT_MFMA_16:
-        err = sgemm::launch_mfma(forced(MfmaTile::T16), MfmaPath::Auto, p, va, vb, s);
+        err = sgemm::launch_mfma(forced(MfmaTile::T16), MfmaPath::Auto, p, w, s);
         break;
       case SGEMM_VARIANT_MFMA_STAGED:
-        err = sgemm::launch_mfma(autotile, MfmaPath::Staged, p, va, vb, s);
+        err = sgemm::launch_mfma(autotile, MfmaPath::Staged, p, w, s);
         break;
       case SGEMM_VARIANT_MFMA_UNPADDED:
-        err = sgemm::launch_mfma(autotile, MfmaPath::Unpadded, p, va, vb, s);
+        err = sgemm::launch_mfma(autotile, MfmaPath::Unpadded, p, w, s);
         break;
       case SGEMM_VARIANT_MFMA_DWORD:
         // 4-byte loads for both operands whatever their alignment.
-        err = sgemm::launch_mfma(autotile, MfmaPath::Auto, p, false, false, s);
+        err = sgemm::launch_mfma(autotile, MfmaPath::Auto, p, sgemm::LoadWidths{}, s);
         break;
       case SGEMM_VARIANT_MFMA_SERIAL:
-        err = sgemm::launch_mfma(autotile, MfmaPath::Serial, p, va, vb, s);
+        err = sgemm::launch_mfma(autotile, MfmaPath::Serial, p, w, s);
         if (err == hipErrorInvalidValue) return SGEMM_ERR_TOO_LARGE;  // no register-staged form
         break;
       default:
-        err = sgemm::launch_mfma(autotile, MfmaPath::Auto, p, va, vb, s);
+        err = sgemm::launch_mfma(autotile, MfmaPath::Auto, p, w, s);
         break;
     }
   }
@@ -254,17 +273,16 @@ int sgemm_phase_times(int64_t M, int64_t N, int64_t K, const float *A, int64_t l
   p.ldb = ldb;
   p.C = C;
   p.ldc = ldc;
-  const bool va = aligned16(A) && lda % 4 == 0 && K % 4 == 0;
-  const bool vb = aligned16(B) && ldb % 4 == 0 && N % 4 == 0;
+  const sgemm::LoadWidths w = load_widths(false, false, M, N, K, A, lda, 0, B, ldb, 0);
   const sgemm::TileChoice tile = sgemm::choose_mfma_tile(M, N, K, di.cus);
   long wgs = 0;
-  hipError_t err = sgemm::launch_mfma_phases(tile, p, va, vb, &wgs, nullptr);  // count only
+  hipError_t err = sgemm::launch_mfma_phases(tile, p, w, &wgs, nullptr);  // count only
   if (err == hipErrorInvalidValue) return SGEMM_ERR_TOO_LARGE;
   *workgroups = wgs;
   if (times == nullptr) return SGEMM_OK;
   if (times_len < 8 * (int64_t)wgs) return SGEMM_ERR_INVALID_VALUE;
   p.phases = reinterpret_cast<unsigned long long *>(times);
-  err = sgemm::launch_mfma_phases(tile, p, va, vb, &wgs, reinterpret_cast<hipStream_t>(stream));
+  err = sgemm::launch_mfma_phases(tile, p, w, &wgs, reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 
@@ -318,12 +336,10 @@ int sgemm_run_strided_batched(int transA, int transB, int64_t M, int64_t N, int6
   if (!reads_ab) {
     err = sgemm::launch_scale(p, s);  // C = beta C (zeros when beta == 0)
   } else {
-    // 16-byte loads need 16-byte aligned bases, strides and leading
-    // dimensions, and a stored width that is a multiple of 4.
-    const bool va = aligned16(A) && lda % 4 == 0 && strideA % 4 == 0 && a_cols % 4 == 0;
-    const bool vb = aligned16(B) && ldb % 4 == 0 && strideB % 4 == 0 && b_cols % 4 == 0;
+    const sgemm::LoadWidths w =
+        load_widths(transA != 0, transB != 0, M, N, K, A, lda, strideA, B, ldb, strideB);
     const sgemm::TileChoice tile = sgemm::choose_mfma_tile(M, N, K, di.cus, batch);
-    err = sgemm::launch_mfma_general(tile, p, transA, transB, va, vb, s);
+    err = sgemm::launch_mfma_general(tile, p, transA, transB, w, s);
     if (err == hipErrorInvalidValue) return SGEMM_ERR_TOO_LARGE;
   }
   return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;

@@ -84,22 +84,32 @@ struct TileGeometry {
 };
 TileGeometry tile_geometry(TileChoice tile, bool wide, long K);
 
-// Matrix-core product.  va / vb: A / B qualify for 128-bit loads.
-hipError_t launch_mfma(TileChoice tile, MfmaPath path, const GemmArgs &p, bool va, bool vb,
+// Which operands take 16-byte loads.  a16 / b16: A / B qualify for the
+// small-product and register-staged kernels (16-byte aligned, leading
+// dimension and stored width multiples of 4).  a_dma / b_dma: A / B qualify
+// for the buffer-to-LDS kernel, which needs only dword alignment, and a
+// stored width that is a multiple of 4 where its 16-byte chunks run along m
+// or n (A stored transposed, B as given); all false forces 4-byte loads.
+struct LoadWidths {
+  bool a16 = false, b16 = false, a_dma = false, b_dma = false;
+};
+
+// Matrix-core product.
+hipError_t launch_mfma(TileChoice tile, MfmaPath path, const GemmArgs &p, LoadWidths w,
                        hipStream_t stream);
 
 // General product C = alpha op(A) op(B) + beta C over p.batch products on
 // the buffer-to-LDS kernel (ta / tb: A / B stored transposed).  Returns
 // hipErrorInvalidValue if a slice's offsets do not fit a buffer descriptor.
-hipError_t launch_mfma_general(TileChoice tile, const GemmArgs &p, bool ta, bool tb, bool va,
-                               bool vb, hipStream_t stream);
+hipError_t launch_mfma_general(TileChoice tile, const GemmArgs &p, bool ta, bool tb, LoadWidths w,
+                               hipStream_t stream);
 
 // sgemm_run's computation of the plain product with phase timestamps in
 // p.phases (8 per work-group); *workgroups receives the launch's work-group
 // count.  With p.phases null nothing is launched.  hipErrorInvalidValue if a
 // slice's offsets do not fit a buffer descriptor.
-hipError_t launch_mfma_phases(TileChoice tile, const GemmArgs &p, bool va, bool vb,
-                              long *workgroups, hipStream_t stream);
+hipError_t launch_mfma_phases(TileChoice tile, const GemmArgs &p, LoadWidths w, long *workgroups,
+                              hipStream_t stream);
 
 // Small-product kernel (mfma_small.hip) over p.batch products: 16 x 16 tiles,
 // four k sets of one wave, operands loaded straight into registers (ta / tb:

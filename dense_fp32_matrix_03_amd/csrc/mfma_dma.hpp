@@ -35,12 +35,21 @@
 // Edges.  The buffer descriptor's range check turns a load at an offset
 // past num_records into zeros; an element outside op(A) (M x K) or op(B)
 // (K x N) is given such an offset, so ragged tiles and the K tail are
-// zero-filled by the hardware.  In the K-tail slice an operand whose k runs
-// along its stored rows needs no per-load test: num_records ends its window
-// after the last valid row.  An operand that is 16-byte aligned with a
-// leading dimension and a stored width that are multiples of 4 is fetched in
-// 16-byte chunks (64 lanes x 16 B = one 1 KiB block per instruction); any
-// other operand in single floats (256 B per instruction).
+// zero-filled by the hardware.  With a ragged K the partial last slice is
+// computed first, so its loads, the only ones that need a K test, go out in
+// the prologue: an operand whose k runs along its stored rows ends its
+// window after the last valid row through num_records, the other one
+// compares each load's k index.
+//
+// Load width.  An operand is fetched in 16-byte chunks (64 lanes x 16 B =
+// one 1 KiB block per instruction) or in single floats (256 B per
+// instruction).  A 16-byte chunk needs only a dword-aligned address, and it
+// fills the same LDS image as four 4-byte loads, so the bits do not depend
+// on the width (tested from every row offset mod 16 bytes).  Where
+// the chunks run along m or n (A transposed, B as given) the stored width
+// must be a multiple of 4, so that no chunk straddles the edge of op(A) or
+// op(B); where they run along k, the partial last slice takes 4-byte loads
+// when K % 4 != 0.
 #pragma once
 
 #include <type_traits>
@@ -160,7 +169,8 @@ struct SliceGeom {
 };
 
 // TA / TB: A / B are stored transposed (op(A) = A^T, op(B) = B^T).
-// VA / VB: A / B take 16-byte loads.  KFULL: K % BK == 0.
+// VA / VB: A / B take 16-byte loads.  KFULL: K % BK == 0 (otherwise the
+// partial last slice is computed first).
 // KSPLIT: the work-group runs KSPLIT sets of WM x WN waves over the same
 // tile; set q takes the k groups g with g % KSPLIT == q of every slice, and
 // the sets' partial sums are added in the order 0, 1, .., KSPLIT - 1 through
@@ -256,8 +266,11 @@ mfma_gemm_dma_kernel(GemmArgs p, TileMap tmap) {
   // reduction (per set, the registers of the other sets).
   constexpr int kRedSlot = NWT * FM * FN * 16 * kWave;
   __shared__ __attribute__((aligned(1024))) float Red[KSPLIT > 1 ? (KSPLIT - 1) * kRedSlot : 1];
-  // Landing area of the spare loads (zeros, never read).
-  __shared__ __attribute__((aligned(1024))) float Dump[GA::SPARE || GB::SPARE ? 4 * kWave : 1];
+  // Landing area of the spare loads (zeros, never read), including those of
+  // the 4-byte loads of a ragged K's tail slice.
+  constexpr bool kSpare = GA::SPARE || GB::SPARE || SliceGeom<BM, BK, TA, false, SWZ, NW>::SPARE ||
+                          SliceGeom<BN, BK, !TB, false, SWZ, NW>::SPARE;
+  __shared__ __attribute__((aligned(1024))) float Dump[kSpare ? 4 * kWave : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -278,16 +291,14 @@ mfma_gemm_dma_kernel(GemmArgs p, TileMap tmap) {
 
   // Per-lane byte offsets relative to the slice origin.  Elements outside
   // op(A)'s rows (M) or op(B)'s columns (N) get the out-of-range offset once
-  // and for all; the K tail is handled per slice.
+  // and for all; the K tail is handled by the one slice that has it.
   unsigned offA[GA::NBW], offB[GB::NBW];
-  int kofA[GA::NBW], kofB[GB::NBW];  // k index of each load within a slice
 #pragma unroll
   for (int q = 0; q < GA::NBW; ++q) {
     int row, col;
     GA::elem(wave, lane, q, row, col);
     offA[q] = m0 + GA::mnof(row, col) < p.M ? (unsigned)(row * p.lda + col) * 4u : kOutOfRange;
     if constexpr (GA::SPARE) offA[q] = wave + q * NW < GA::NB ? offA[q] : kOutOfRange;
-    kofA[q] = GA::kof(row, col);
   }
 #pragma unroll
   for (int q = 0; q < GB::NBW; ++q) {
@@ -295,48 +306,87 @@ mfma_gemm_dma_kernel(GemmArgs p, TileMap tmap) {
     GB::elem(wave, lane, q, row, col);
     offB[q] = n0 + GB::mnof(row, col) < p.N ? (unsigned)(row * p.ldb + col) * 4u : kOutOfRange;
     if constexpr (GB::SPARE) offB[q] = wave + q * NW < GB::NB ? offB[q] : kOutOfRange;
-    kofB[q] = GB::kof(row, col);
   }
 
-  // Issue the loads of slice t into LDS stage S.  A slice at or past the end
-  // of K gets descriptors with no records: every lane reads out of range, so
-  // nothing is fetched and zeros land in a stage nobody reads again.  This
-  // keeps the slice body free of branches, so the scheduler can interleave
-  // these loads with matrix-core instructions.
+  // Slice order.  With a ragged K (not KFULL) the partial last slice is
+  // computed first: its loads go out in the prologue, so every slice whose
+  // loads the main loop issues is a whole one and needs no K test.  Position
+  // u of the order is slice u - 1 for u >= 1 (slice u with KFULL).  A
+  // position at or past nk gets descriptors with no records: every lane reads
+  // out of range, so nothing is fetched and zeros land in a stage nobody
+  // reads again.  This keeps the slice body free of branches, so the
+  // scheduler can interleave these loads with matrix-core instructions.
   const int nk = (p.K + BK - 1) / BK;
-  auto dma = [&](auto S, int t) {
+  auto rsrc = [](const float *base, int records) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, records,
+                                             kRawBufferWord3);
+  };
+  auto origin_a = [&](int k0) { return TA ? Ab + (long)k0 * p.lda + m0 : Ab + (long)m0 * p.lda + k0; };
+  auto origin_b = [&](int k0) { return TB ? Bb + (long)n0 * p.ldb + k0 : Bb + (long)k0 * p.ldb + n0; };
+  auto dma = [&](auto S, int u) {
     float *as = stage_a(S);
     float *bs = stage_b(S);
-    const int k0 = t < nk ? t * BK : 0;
-    const int records = t < nk ? kBufferRecords : 0;
-    // K tail (not KFULL): an operand whose k runs along its stored rows ends
-    // its window after the last valid row, through the descriptor's
-    // num_records; the other operand compares each load's k index.
-    const int kl = p.K - k0 < BK ? p.K - k0 : BK;  // valid k in this slice
-    const int rec_a = KFULL || !GA::KR ? records : (t < nk ? kl * (int)p.lda * 4 : 0);
-    const int rec_b = KFULL || !GB::KR ? records : (t < nk ? kl * (int)p.ldb * 4 : 0);
-    const float *abase = TA ? Ab + (long)k0 * p.lda + m0 : Ab + (long)m0 * p.lda + k0;
-    const float *bbase = TB ? Bb + (long)n0 * p.ldb + k0 : Bb + (long)k0 * p.ldb + n0;
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(abase), 0, rec_a, kRawBufferWord3);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(bbase), 0, rec_b, kRawBufferWord3);
+    const int t = KFULL ? u : u - 1;
+    const int k0 = u < nk ? t * BK : 0;
+    const int records = u < nk ? kBufferRecords : 0;
+    const float *abase = origin_a(k0);
+    const float *bbase = origin_b(k0);
+    const __amdgpu_buffer_rsrc_t ra = rsrc(abase, records);
+    const __amdgpu_buffer_rsrc_t rb = rsrc(bbase, records);
 #pragma unroll
     for (int q = 0; q < GA::NBW; ++q) {
-      unsigned off = offA[q];
-      if constexpr (!KFULL && !GA::KR) off = kofA[q] < kl ? off : kOutOfRange;
       float *dst = as + (wave + q * NW) * GA::FPB;
       if constexpr (GA::SPARE) dst = wave + q * NW < GA::NB ? dst : Dump;
-      lds_dma<VA>(ra, dst, off);
+      lds_dma<VA>(ra, dst, offA[q]);
     }
 #pragma unroll
     for (int q = 0; q < GB::NBW; ++q) {
-      unsigned off = offB[q];
-      if constexpr (!KFULL && !GB::KR) off = kofB[q] < kl ? off : kOutOfRange;
       float *dst = bs + (wave + q * NW) * GB::FPB;
       if constexpr (GB::SPARE) dst = wave + q * NW < GB::NB ? dst : Dump;
-      lds_dma<VB>(rb, dst, off);
+      lds_dma<VB>(rb, dst, offB[q]);
     }
+  };
+
+  // The partial last slice (K % BK valid k), into stage 0.  An operand whose
+  // k runs along its stored rows ends its window after the last valid row,
+  // through the descriptor's num_records.  The other one compares each
+  // load's k index with the valid count; where K % 4 != 0 its 16-byte chunk
+  // at the end of K would hold k past K, so that operand takes 4-byte loads
+  // in this slice (they fill the same LDS image, so the bits do not change).
+  auto tail_operand = [&](auto geom, auto wide, float *stage, const float *origin, long ld,
+                          int mn0, int mn_count, int kl) {
+    using Gm = decltype(geom);
+    constexpr bool W = decltype(wide)::value;
+    const int rec = Gm::KR ? kl * (int)ld * 4 : kBufferRecords;
+    const __amdgpu_buffer_rsrc_t r = rsrc(origin, rec);
+#pragma unroll
+    for (int q = 0; q < Gm::NBW; ++q) {
+      int row, col;
+      Gm::elem(wave, lane, q, row, col);
+      bool in = mn0 + Gm::mnof(row, col) < mn_count && (Gm::KR || Gm::kof(row, col) < kl);
+      float *dst = stage + (wave + q * NW) * Gm::FPB;
+      if constexpr (Gm::SPARE) {
+        in = in && wave + q * NW < Gm::NB;
+        dst = wave + q * NW < Gm::NB ? dst : Dump;
+      }
+      lds_dma<W>(r, dst, in ? (unsigned)(row * ld + col) * 4u : kOutOfRange);
+    }
+  };
+  auto dma_tail = [&](auto S) {
+    const int k0 = (nk - 1) * BK;
+    const int kl = p.K - k0;
+    using GAn = SliceGeom<BM, BK, TA, false, SWZ, NW>;
+    using GBn = SliceGeom<BN, BK, !TB, false, SWZ, NW>;
+    if (VA && !GA::KR && p.K % 4 != 0)
+      tail_operand(GAn(), std::false_type(), stage_a(S), origin_a(k0), p.lda, m0, p.M, kl);
+    else
+      tail_operand(GA(), std::integral_constant<bool, VA>(), stage_a(S), origin_a(k0), p.lda, m0,
+                   p.M, kl);
+    if (VB && !GB::KR && p.K % 4 != 0)
+      tail_operand(GBn(), std::false_type(), stage_b(S), origin_b(k0), p.ldb, n0, p.N, kl);
+    else
+      tail_operand(GB(), std::integral_constant<bool, VB>(), stage_b(S), origin_b(k0), p.ldb, n0,
+                   p.N, kl);
   };
 
   // Operand read offsets (floats).  In a k-contiguous image, row
@@ -470,7 +520,12 @@ mfma_gemm_dma_kernel(GemmArgs p, TileMap tmap) {
     }
   };
 
-  static_for<NST>([&](auto S) { dma(S, decltype(S)::value); });
+  static_for<NST>([&](auto S) {
+    if constexpr (!KFULL && decltype(S)::value == 0)
+      dma_tail(S);
+    else
+      dma(S, decltype(S)::value);
+  });
   // Slice 0 has landed; slices 1 .. NST-1 may still fly.
   if constexpr (SCHED == 2)
     dma_barrier();

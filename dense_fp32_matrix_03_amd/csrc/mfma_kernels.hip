@@ -145,43 +145,76 @@ TileGeometry tile_geometry(TileChoice tile, bool wide, long K) {
   return {g.bm, g.bn, g.bk, g.ksets};
 }
 
-hipError_t launch_mfma(TileChoice tile, MfmaPath path, const GemmArgs &p, bool va, bool vb,
+// Load widths of the buffer-to-LDS kernel for configuration c and depth K.
+// The 64 x 96 tile (12 waves, three per SIMD) keeps 16-byte loads to
+// operands that the stricter rule of the other kernels admits (w.a16,
+// w.b16): with 16-byte A loads wherever the rule of the buffer-to-LDS
+// kernel allows them it ran slower than with 4-byte loads on most shapes
+// measured (HIP events, three alternations on one box: 1000 x 1500 x 1199
+// 33.6 against 31.7 us, 960 x 1600 x 777 22.9 against 21.9), while the
+// other tiles gained (512 x 512 x 1199 8.8 against 10.4 us, 800 x 1280 x
+// 1199 22.5 against 24.9, 2048 x 2048 x 2047 118.6 against 125.4).  With a
+// ragged K (the partial slice computed first) it also takes 4-byte loads
+// from K = 960 on, where they beat 16-byte loads from 16-byte aligned
+// operands (1000 x 1500 x K, two sweeps: K = 1000 26.6 against 27.9 us,
+// 1200 30.8 against 33.4, 2000 48.0-48.9 against 52.7; 1200 x 1200 x 1200
+// 31.6 against 33.0), as they do not at shorter K (700 20.0-20.4 against
+// 19.3-19.7, 784 21.9-22.1 against 21.2-21.4) nor with K a multiple of 32
+// (1600: 43.7 against 42.7).
+static void dma_widths(DmaCfg c, LoadWidths w, long K, bool &va, bool &vb) {
+  if (c == DmaCfg::C64x96) {
+    const bool wide = K % 32 == 0 || K < 960;
+    va = wide && w.a16;
+    vb = wide && w.b16;
+  } else {
+    va = w.a_dma;
+    vb = w.b_dma;
+  }
+}
+
+hipError_t launch_mfma(TileChoice tile, MfmaPath path, const GemmArgs &p, LoadWidths w,
                        hipStream_t stream) {
-  if (path == MfmaPath::Staged) return launch_staged(tile.tile, true, p, va, vb, stream);
+  if (path == MfmaPath::Staged) return launch_staged(tile.tile, true, p, w.a16, w.b16, stream);
   if (tile.tile == MfmaTile::T16 && path != MfmaPath::Unpadded)
-    return launch_small(p, false, false, va, vb, stream);
-  const DmaCfg c = dma_cfg(tile, va && vb);
+    return launch_small(p, false, false, w.a16, w.b16, stream);
+  const DmaCfg c = dma_cfg(tile, w.a_dma && w.b_dma);
   const DmaGeom g = dma_geom(c);
   // A slice whose offsets pass a buffer descriptor's 32-bit range takes the
   // register-staged kernel (64-bit addressing).
   if (!dma_offsets_fit(g.bm, p.lda, g.bk, p.ldb)) {
     if (path == MfmaPath::Serial) return hipErrorInvalidValue;
-    return launch_staged(tile.tile, path != MfmaPath::Unpadded, p, va, vb, stream);
+    return launch_staged(tile.tile, path != MfmaPath::Unpadded, p, w.a16, w.b16, stream);
   }
+  bool va, vb;
+  dma_widths(c, w, p.K, va, vb);
   if (path == MfmaPath::Serial)
     return launch_dma_layout<false, false, true, false, 2>(c, p, va, vb, stream);
   if (path == MfmaPath::Unpadded) return launch_dma_layout<false, false, false>(c, p, va, vb, stream);
   return launch_dma_layout<false, false, true>(c, p, va, vb, stream);
 }
 
-hipError_t launch_mfma_phases(TileChoice tile, const GemmArgs &p, bool va, bool vb,
-                              long *workgroups, hipStream_t stream) {
+hipError_t launch_mfma_phases(TileChoice tile, const GemmArgs &p, LoadWidths w, long *workgroups,
+                              hipStream_t stream) {
   if (tile.tile == MfmaTile::T16) {
     *workgroups = small_workgroups(p.M, p.N, 1);
-    return p.phases == nullptr ? hipSuccess : launch_small_phases(p, va, stream);
+    return p.phases == nullptr ? hipSuccess : launch_small_phases(p, w.a16, stream);
   }
-  const DmaCfg c = dma_cfg(tile, va && vb);
+  const DmaCfg c = dma_cfg(tile, w.a_dma && w.b_dma);
   const DmaGeom g = dma_geom(c);
   if (!dma_offsets_fit(g.bm, p.lda, g.bk, p.ldb)) return hipErrorInvalidValue;
   *workgroups = (long)((p.M + g.bm - 1) / g.bm) * ((p.N + g.bn - 1) / g.bn);
   if (p.phases == nullptr) return hipSuccess;
+  bool va, vb;
+  dma_widths(c, w, p.K, va, vb);
   return launch_dma_layout<false, false, true, true>(c, p, va, vb, stream);
 }
 
-hipError_t launch_mfma_general(TileChoice tile, const GemmArgs &p, bool ta, bool tb, bool va,
-                               bool vb, hipStream_t stream) {
-  if (tile.tile == MfmaTile::T16) return launch_small(p, ta, tb, va, vb, stream);
-  const DmaCfg c = dma_cfg(tile, !ta && !tb && va && vb);
+hipError_t launch_mfma_general(TileChoice tile, const GemmArgs &p, bool ta, bool tb, LoadWidths w,
+                               hipStream_t stream) {
+  if (tile.tile == MfmaTile::T16) return launch_small(p, ta, tb, w.a16, w.b16, stream);
+  const DmaCfg c = dma_cfg(tile, !ta && !tb && w.a_dma && w.b_dma);
+  bool va, vb;
+  dma_widths(c, w, p.K, va, vb);
   const DmaGeom g = dma_geom(c);
   if (!dma_offsets_fit(ta ? g.bk : g.bm, p.lda, tb ? g.bn : g.bk, p.ldb))
     return hipErrorInvalidValue;

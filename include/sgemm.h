@@ -27,8 +27,11 @@
  * Pointers and ownership.  A, B and C are device pointers owned by the
  * caller; the library allocates no memory per call and keeps no pointer
  * after a call returns.  C must not overlap A or B.  Any 4-byte alignment is
- * accepted; 16-byte alignment with leading dimensions and widths that are
- * multiples of 4 enables 128-bit loads.
+ * accepted.  The matrix-core path fetches an operand in 16-byte chunks from
+ * any 4-byte aligned address wherever no chunk would cross the edge of the
+ * operand (the stored width a multiple of 4 where the chunks run along m or
+ * n); the other kernels need 16-byte alignment and leading dimensions and
+ * widths that are multiples of 4 for 16-byte loads.
  *
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
  * stream of the current device).  Calls are asynchronous: they return once
@@ -78,9 +81,11 @@ extern "C" {
  * with 8x8 outputs per thread over 128x128x16 blocks (chapter sections 一
  * and 二), and that with a double-buffered LDS pipeline (chapter section
  * 四).  SGEMM_VARIANT_MFMA is the matrix-core path that sgemm_run uses:
- * operand slices reach LDS by buffer-to-LDS loads, 16 bytes per lane where
- * the operand is 16-byte aligned with a leading dimension and width that are
- * multiples of 4, else 4 bytes; only an operand whose leading dimension puts
+ * operand slices reach LDS by buffer-to-LDS loads, 16 bytes per lane (from
+ * any 4-byte aligned address; 4 bytes in the partial last K slice when
+ * K % 4 != 0, and on the 64 x 96 tile for operands that are not 16-byte
+ * aligned with a leading dimension and width that are multiples of 4, or
+ * once a ragged K reaches 960), else 4 bytes; only an operand whose leading dimension puts
  * one slice beyond 2 GiB is fetched through registers instead.  sgemm_run
  * picks the block tile (256 x 256, 128 x 128, 64 x 96, 64 x 64, 32 x 64 or
  * 32 x 32) that loses the least matrix-core time to partly filled rounds of

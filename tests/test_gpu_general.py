@@ -74,7 +74,8 @@ def test_general_integer_exact_2048(ta, tb):
 
 
 @pytest.mark.parametrize("ta,tb", LAYOUTS[1:], ids=LAYOUT_IDS[1:])
-@pytest.mark.parametrize("shape", [(1024, 1024, 1024), (1000, 1500, 780), (300, 260, 100)],
+@pytest.mark.parametrize("shape", [(1024, 1024, 1024), (1000, 1500, 780), (300, 260, 100),
+                                   (1000, 1500, 777), (332, 261, 101)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_transposed_storage_gives_identical_bits(ta, tb, shape):
     """The matrix-core sequence does not depend on how an operand is stored:

@@ -324,7 +324,9 @@ def test_padded_leading_dimensions(variant):
 
 @pytest.mark.parametrize("variant", ["mfma", "mfma_128", "lds", "dbuf", "mfma_16", "mfma_64x96"])
 def test_misaligned_pointers(variant):
-    """Operands that start 4 bytes past a 16-byte boundary take the 32-bit path."""
+    """Operands that start 4 or 12 bytes past a 16-byte boundary: 16-byte
+    buffer-to-LDS loads from dword-aligned addresses, 4-byte loads in the
+    other kernels."""
     import torch
     M, N, K = 130, 100, 68
     g = np.random.default_rng(37)
@@ -344,6 +346,82 @@ def test_misaligned_pointers(variant):
     r = oracle.check(C, Cref, Sabs)
     assert r.ok, str(r)
 
+
+
+def _unaligned_rows(A, lda, shift):
+    """A's rows lda floats apart, `shift` floats into a NaN-filled device
+    buffer (NaN in the padding past K and after the last row); returns the
+    buffer and the byte address of A's first element."""
+    M, K = A.shape
+    host = np.full(shift + M * lda + 8, np.nan, np.float32)
+    host[shift:shift + M * lda].reshape(M, lda)[:, :K] = A
+    buf = _dev(host)
+    return buf, buf.data_ptr() + 4 * shift
+
+
+def _run_at(variant, M, N, K, a_ptr, lda, dB):
+    """One product with A given by address; C inside NaN guards, checked."""
+    import torch
+    dC = torch.full((GUARD_LEAD + (M + GUARD_ROWS) * N,), float("nan"), dtype=torch.float32,
+                    device="cuda")
+    sg.sgemm_run_variant(variant, M, N, K, a_ptr, lda, dB, N, dC.data_ptr() + 4 * GUARD_LEAD, N)
+    torch.cuda.synchronize()
+    host = dC.cpu().numpy()
+    _check_guards(host, M, N, N)
+    return host[GUARD_LEAD:GUARD_LEAD + M * N].reshape(M, N)
+
+
+# A's rows off the 16-byte grid (an odd lda, or a base 4, 8 or 12 bytes past
+# it) with K % 4 = 0, 1, 2 and 3, on the shapes where sgemm_run takes each
+# buffer-to-LDS configuration: the ragged workload's 64 x 96 tile, 32 x 64,
+# 64 x 64 in two k sets (32- and 64-float slices), 32 x 32, 128 x 128, and
+# an odd-sized product.  (M, N, K, lda, shift in floats.)
+UNALIGNED_ROWS = [(1000, 1500, 777, 777, 0), (1000, 1500, 776, 777, 0), (800, 1280, 778, 781, 1),
+                  (1024, 1024, 1024, 1025, 3), (896, 896, 1301, 1303, 2), (512, 512, 515, 517, 1),
+                  (2048, 2048, 515, 515, 0), (129, 67, 45, 47, 1)]
+
+
+@pytest.mark.parametrize("M,N,K,lda,shift", UNALIGNED_ROWS, ids=lambda v: str(v))
+def test_unaligned_rows_take_16_byte_loads(M, N, K, lda, shift):
+    """sgemm_run fetches rows of A that start off the 16-byte grid in 16-byte
+    chunks, and a partial last K slice with K % 4 != 0 in 4-byte loads; both
+    fill the LDS image that 4-byte loads fill, so the result has the bits of
+    the forced 4-byte variant, meets the tolerance, and leaves C's
+    surroundings untouched (NaN in A's padding never reaches C)."""
+    g = np.random.default_rng(M + 3 * K + 7 * lda + shift)
+    A = inputs.uniform(g, (M, K))
+    B = inputs.uniform(g, (K, N))
+    buf, a_ptr = _unaligned_rows(A, lda, shift)
+    dB = _dev(B)
+    C = _run_at("mfma", M, N, K, a_ptr, lda, dB)
+    C4 = _run_at("mfma_dword", M, N, K, a_ptr, lda, dB)
+    assert C.tobytes() == C4.tobytes()
+    Cref, Sabs = oracle.sgemm_f64(A, B)
+    r = oracle.check(C, Cref, Sabs)
+    assert r.ok and r.usage < 0.05, str(r)
+
+
+@pytest.mark.parametrize("variant", ["mfma_32", "mfma_32x64", "mfma_64", "mfma_64x96", "mfma_128",
+                                     "mfma_256", "mfma_serial"])
+@pytest.mark.parametrize("M,N,K,lda,shift", [(333, 257, 260, 263, 1), (600, 700, 777, 777, 0),
+                                             (300, 520, 1299, 1301, 3)], ids=lambda v: str(v))
+def test_unaligned_rows_every_tile(variant, M, N, K, lda, shift):
+    """Each buffer-to-LDS tile gives the same bits from A's rows off the
+    16-byte grid as from a copy whose rows are 16-byte aligned (the same
+    tile, K slices and matrix-core sequence), and meets the tolerance."""
+    g = np.random.default_rng(K * 5 + lda + shift)
+    A = inputs.uniform(g, (M, K))
+    B = inputs.uniform(g, (K, N))
+    lda4 = (K + 3) // 4 * 4
+    buf, a_ptr = _unaligned_rows(A, lda, shift)
+    buf4, a4_ptr = _unaligned_rows(A, lda4, 0)
+    dB = _dev(B)
+    C = _run_at(variant, M, N, K, a_ptr, lda, dB)
+    C4 = _run_at(variant, M, N, K, a4_ptr, lda4, dB)
+    assert C.tobytes() == C4.tobytes()
+    Cref, Sabs = oracle.sgemm_f64(A, B)
+    r = oracle.check(C, Cref, Sabs)
+    assert r.ok and r.usage < 0.05, str(r)
 
 # sgemm_run's tile rule, restated: the tile that loses the least matrix-core
 # time to partly filled rounds of work-groups and to tile area outside C
