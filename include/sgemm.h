@@ -81,12 +81,13 @@ extern "C" {
  * with 8x8 outputs per thread over 128x128x16 blocks (chapter sections 一
  * and 二), and that with a double-buffered LDS pipeline (chapter section
  * 四).  SGEMM_VARIANT_MFMA is the matrix-core path that sgemm_run uses:
- * operand slices reach LDS by buffer-to-LDS loads, 16 bytes per lane (from
- * any 4-byte aligned address; 4 bytes in the partial last K slice when
- * K % 4 != 0, and on the 64 x 96 tile for operands that are not 16-byte
- * aligned with a leading dimension and width that are multiples of 4, or
- * once a ragged K reaches 960), else 4 bytes; only an operand whose leading dimension puts
- * one slice beyond 2 GiB is fetched through registers instead.  sgemm_run
+ * operand slices reach LDS by buffer-to-LDS loads of 16 bytes per lane
+ * from any 4-byte aligned address, and of 4 bytes in the partial last K
+ * slice when K % 4 != 0 and, on the 64 x 96 tile, for operands that are not
+ * 16-byte aligned with a leading dimension and width that are multiples of
+ * 4 or once a ragged K reaches 960; only an operand whose leading
+ * dimension puts one slice beyond 2 GiB is fetched through registers
+ * instead.  sgemm_run
  * picks the block tile (256 x 256, 128 x 128, 64 x 96, 64 x 64, 32 x 64 or
  * 32 x 32) that loses the least matrix-core time to partly filled rounds of
  * work-groups and to tile area outside C, the larger one when two come
